@@ -1,0 +1,264 @@
+"""Pins for oracle.nvfp4 (two-level quantize / dequantize).  No GPU.
+
+What pins it, other than itself:
+* the page's recipe and audit (golden fixtures): 16-element blocks, 4.5 bits,
+  scales finite, positive, at most 448, the largest exactly 448, and a global
+  scale of the audit's order for weights of spread 0.02;
+* closed forms: exact round trip of representable tensors, sign symmetry,
+  all-zero and degenerate tensors;
+* brute force in exact rationals on tiny tensors: every block scale is the
+  nearest E4M3 value to its float32 target, every code the nearest E2M1 value
+  to its scaled element, and the scale makes the block's largest element land
+  within the E2M1 range.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4 as Q
+from oracle.formats import E2M1_MAGNITUDES, E4M3_NONNEG, e2m1_decode, e4m3_decode
+from moe_nvfp4_quantize_amd import workloads as W
+
+
+def _recipe(golden):
+    return dict(r.split(": ") for r in golden("nvfp4_recipe.txt"))
+
+
+def _c1():
+    x, w = W.linear_inputs("linear_16x512")
+    return x.numpy(), w.numpy()
+
+
+def _tensors():
+    x, w = _c1()
+    rng = np.random.default_rng(11)
+    skewed = (rng.standard_normal((64, 256)) * np.exp(rng.standard_normal(256))).astype(np.float32)
+    tiny = (rng.standard_normal((8, 64)) * 1e-20).astype(np.float32)
+    return dict(x=x, w=w, skewed=skewed, tiny=tiny)
+
+
+def test_block_size_and_effective_bits(golden):
+    rec = _recipe(golden)
+    assert Q.BLOCK == int(rec["block_size"]) and rec["block_axis"] == "-1"
+    for t in _tensors().values():
+        q, s, g = Q.quantize(t)
+        assert q.shape == (t.shape[0], t.shape[1] // 2)
+        assert s.shape == (t.shape[0], t.shape[1] // 16)
+        assert Q.effective_bits(q, s, t.size) == float(rec["effective_bits"])
+
+
+def test_scales_finite_positive_max_448(golden):
+    audit = dict(r.split(": ") for r in golden("scale_audit.txt"))
+    for name, t in _tensors().items():
+        q, s, g = Q.quantize(t)
+        sv = e4m3_decode(s)
+        assert np.all(np.isfinite(sv)) and np.all(sv > 0), name
+        assert sv.max() == float(audit["scale_max"]), name
+        assert np.isfinite(g) and g > 0, name
+
+
+def test_global_scale_magnitude_matches_audit(golden):
+    """Weights of spread 0.02 give a global scale of the audit's order (about 2e-5)."""
+    audit = dict(r.split(": ") for r in golden("scale_audit.txt"))
+    smallest = float(audit["scale_min_approx"])
+    _, w = _c1()
+    g = Q.global_scale(w)
+    assert smallest / 3 < g < smallest * 3
+
+
+def test_amax_element_maps_to_six_and_scale_448():
+    for t in _tensors().values():
+        q, s, g = Q.quantize(t)
+        codes = Q.unpack_codes(q)
+        r, c = np.unravel_index(np.argmax(np.abs(t)), t.shape)
+        assert codes[r, c] & 7 == 7
+        assert s[r, c // 16] == 0x7E
+
+
+def test_normal_scale_blocks_reach_six():
+    """A block whose scale is an E4M3 normal has its largest element at code +-6.
+
+    E4M3 normals carry 3 mantissa bits, so the block scale is within 1/16 of its
+    target and the scaled block max lies in [5.65, 6.4], which rounds to 6.
+    """
+    for t in _tensors().values():
+        q, s, g = Q.quantize(t)
+        codes = Q.unpack_codes(q).reshape(t.shape[0], -1, 16)
+        normal = e4m3_decode(s) >= 2.0 ** -6
+        top = (codes & 7).max(axis=-1)
+        assert np.all(top[normal] == 7)
+
+
+def test_dequantized_error_within_half_step():
+    """In normal-scale blocks |x - x_hat| is at most one unit of s*g.
+
+    The E2M1 grid spacing is at most 2 units (between 4 and 6), so rounding is off
+    by at most 1 unit; saturation of a scaled block max <= 6.4 is off by at most
+    0.4 units.
+    """
+    for t in _tensors().values():
+        q, s, g = Q.quantize(t)
+        xh = Q.dequantize(q, s, g)
+        unit = e4m3_decode(s).astype(np.float64) * np.float64(g)
+        err = np.abs(t.astype(np.float64) - xh).reshape(t.shape[0], -1, 16).max(axis=-1)
+        normal = e4m3_decode(s) >= 2.0 ** -6
+        assert np.all(err[normal] <= unit[normal] * (1 + 1e-6))
+
+
+def _representable(rng, rows, cols, g_exp):
+    """x = e2m1 * e4m3 * 2**g_exp with a +-6 in every block and one block at 448."""
+    nb = cols // 16
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    blk = codes.reshape(rows, nb, 16)
+    pos = rng.integers(0, 16, size=(rows, nb))
+    sign = rng.integers(0, 2, size=(rows, nb)).astype(np.uint8) << 3
+    np.put_along_axis(blk, pos[..., None], (7 | sign)[..., None], axis=-1)
+    s = rng.integers(1, 0x7F, size=(rows, nb)).astype(np.uint8)
+    s[0, 0] = 0x7E
+    g = np.float32(2.0 ** g_exp)
+    x = (e2m1_decode(codes).reshape(rows, nb, 16) * e4m3_decode(s)[..., None]).reshape(rows, cols) * float(g)
+    x32 = x.astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), x)  # exactly representable
+    return x32, Q.pack_codes(codes), s, g
+
+
+@pytest.mark.parametrize("g_exp", [-15, -8, 0, 3])
+def test_round_trip_of_representable_tensor(g_exp):
+    rng = np.random.default_rng(100 + g_exp)
+    x, q0, s0, g0 = _representable(rng, 8, 128, g_exp)
+    q, s, g = Q.quantize(x)
+    assert g == g0
+    np.testing.assert_array_equal(s, s0)
+    # -0 codes (0x8) come back as 0x8 because the sign is kept
+    np.testing.assert_array_equal(q, q0)
+    np.testing.assert_array_equal(Q.dequantize(q, s, g), x.astype(np.float64))
+
+
+def test_every_e4m3_scale_round_trips():
+    """All 126 positive finite scales appear and survive the round trip."""
+    rng = np.random.default_rng(3)
+    x, q0, s0, g0 = _representable(rng, 1, 16 * 127, -4)
+    s0[0, :] = np.concatenate([[0x7E], np.arange(1, 0x7F)])
+    codes = Q.unpack_codes(q0)
+    x = (e2m1_decode(codes).reshape(1, -1, 16) * e4m3_decode(s0)[..., None]).reshape(1, -1) * float(g0)
+    x = x.astype(np.float32)
+    q, s, g = Q.quantize(x)
+    np.testing.assert_array_equal(s, s0)
+    np.testing.assert_array_equal(q, q0)
+
+
+def test_sign_symmetry():
+    for t in _tensors().values():
+        q, s, g = Q.quantize(t)
+        qn, sn, gn = Q.quantize(-t)
+        assert g == gn
+        np.testing.assert_array_equal(s, sn)
+        np.testing.assert_array_equal(Q.unpack_codes(qn), Q.unpack_codes(q) ^ 8)
+
+
+def test_all_zero_and_negative_zero():
+    z = np.zeros((2, 32), dtype=np.float32)
+    q, s, g = Q.quantize(z)
+    assert g == 1.0 and np.all(s == 1) and np.all(q == 0)
+    q, s, g = Q.quantize(-z)
+    assert g == 1.0 and np.all(s == 1) and np.all(q == 0x88)
+
+
+def test_zero_block_gets_smallest_scale():
+    x = np.zeros((1, 48), dtype=np.float32)
+    x[0, 20] = 3.0
+    q, s, g = Q.quantize(x)
+    assert list(s[0]) == [1, 0x7E, 1]
+    codes = Q.unpack_codes(q)[0]
+    assert codes[20] == 7 and np.all(np.delete(codes, 20) == 0)
+
+
+def test_static_global_scale():
+    x, _ = _c1()
+    g_dyn = Q.global_scale(x)
+    q1, s1, g1 = Q.quantize(x, g=g_dyn)
+    q2, s2, g2 = Q.quantize(x)
+    assert g1 == g2 and np.array_equal(q1, q2) and np.array_equal(s1, s2)
+    # a global scale 4096x too small saturates: every non-zero block clamps to 448
+    q3, s3, _ = Q.quantize(x, g=g_dyn / np.float32(4096))
+    assert np.all(s3[np.abs(x).reshape(16, -1, 16).max(-1) > 0] == 0x7E)
+    with pytest.raises(ValueError):
+        Q.quantize(x, g=np.float32(0))
+
+
+def test_rejects_bad_shapes_and_values():
+    with pytest.raises(ValueError):
+        Q.quantize(np.zeros((2, 24), dtype=np.float32))
+    with pytest.raises(ValueError):
+        Q.quantize(np.full((1, 16), np.nan, dtype=np.float32))
+    with pytest.raises(ValueError):
+        Q.quantize(np.full((1, 16), 1e-35, dtype=np.float32))
+
+
+def test_pack_order_low_nibble_first():
+    codes = np.array([[1, 2, 0xF, 0x8]], dtype=np.uint8)
+    assert list(Q.pack_codes(codes)[0]) == [0x21, 0x8F]
+    np.testing.assert_array_equal(Q.unpack_codes(Q.pack_codes(codes)), codes)
+
+
+def _exact_checks(x):
+    """Brute force in exact rationals: each rounding in the quantizer picks a nearest value."""
+    q, s, g = Q.quantize(x)
+    codes = Q.unpack_codes(q)
+    G = Fraction(float(g))
+    amax = max(abs(Fraction(float(v))) for v in x.reshape(-1))
+    if amax:
+        # g is the float32 nearest to amax / 2688
+        assert abs(G - amax / 2688) <= abs(Fraction(float(np.nextafter(g, np.float32(1)))) - amax / 2688)
+        assert abs(G - amax / 2688) <= abs(Fraction(float(np.nextafter(g, np.float32(0)))) - amax / 2688)
+    table = [Fraction(float(v)) for v in E4M3_NONNEG]
+    grid = [Fraction(float(v)) for v in E2M1_MAGNITUDES]
+    rows, cols = x.shape
+    for r in range(rows):
+        for b in range(cols // 16):
+            blk = [Fraction(float(v)) for v in x[r, 16 * b:16 * b + 16]]
+            bmax = max(abs(v) for v in blk)
+            six_g = Fraction(float(np.float32(6.0) * g))
+            target = Fraction(float(np.float32(float(bmax)) / np.float32(float(six_g))))
+            # the float32 target is within half an ulp of the exact quotient
+            assert abs(target - bmax / six_g) <= abs(target) * Fraction(1, 2 ** 24)
+            sv = Fraction(float(e4m3_decode(s[r, b])))
+            t = min(target, Fraction(448))
+            if t <= table[1] / 2:
+                # nearest is zero (ties to the even code 0): clamped to 2**-9
+                assert sv == table[1]
+            else:
+                assert all(abs(sv - t) <= abs(c - t) for c in table)
+            r32 = np.float32(1.0) / np.float32(float(sv) * float(G))
+            for i, v in enumerate(blk):
+                y = Fraction(float(np.float32(float(v)) * r32))
+                a = min(abs(y), Fraction(6))
+                c = codes[r, 16 * b + i]
+                got = grid[c & 7]
+                assert all(abs(got - a) <= abs(m - a) for m in grid)
+                assert (c >> 3) == (1 if np.signbit(np.float32(float(v))) else 0)
+    return q, s, g
+
+
+@pytest.mark.parametrize("shape,seed", [((1, 16), 0), ((2, 32), 1), ((4, 64), 2), ((3, 48), 3)])
+def test_brute_force_tiny(shape, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * np.exp(rng.standard_normal(shape) * 2)).astype(np.float32)
+    x[0, 0] = -x[0, 0]
+    _exact_checks(x)
+
+
+def test_brute_force_c1_rows():
+    x, w = _c1()
+    _exact_checks(x[:2])
+    _exact_checks(w[:2])
+
+
+def test_bf16_inputs_widen_exactly():
+    t = W.random_matrix(4, 64, seed=9, dtype=torch.bfloat16)
+    x32 = t.float().numpy()
+    assert np.array_equal(x32.astype(np.float64), t.double().numpy())
+    Q.quantize(x32)
