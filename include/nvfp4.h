@@ -1,0 +1,199 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 W4A4 quantize, GEMM and routed-expert
+ * MoE kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Format (Qwen3.8-Flash-Next-NVFP4 page, section "Core: the W4A4 two-level
+ * scaling mechanism"): a tensor [rows x cols] is cut into 16-element blocks
+ * along cols (its last dimension).  Each element is a 4-bit E2M1 code, each
+ * block has one E4M3 (E4M3FN, largest value 448) scale, and the tensor has one
+ * FP32 global scale; (16*4 + 8)/16 = 4.5 bits per element ("Why 4.5 bits").
+ *
+ * An NVFP4 tensor at this ABI is three device buffers:
+ *   q  uint8 [rows][cols/2]   two codes per byte, element 2j in bits 3..0 and
+ *                             element 2j+1 in bits 7..4; code bit 3 is the sign
+ *   s  uint8 [rows][cols/16]  E4M3FN scale codes, row-major, always positive
+ *   g  float [1]              decode multiplier: x_hat = e2m1(q) * e4m3(s) * g
+ * Rows of q and s are dense (row strides cols/2 and cols/16 bytes).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless its comment says host.
+ *     The caller owns all memory; the library never allocates or frees device
+ *     memory and never synchronizes: each call validates its arguments on the
+ *     host, enqueues kernels on `stream` and returns.
+ *   - Arguments are validated before any HIP call.  On failure the call returns
+ *     NVFP4_ERR_INVALID_ARG (or NVFP4_ERR_UNSUPPORTED for a valid request this
+ *     build does not implement) and touches no device memory.
+ *   - A failed launch returns NVFP4_ERR_HIP; the HIP error is not cleared.
+ *   - The current HIP device must be a gfx950 GPU, otherwise
+ *     NVFP4_ERR_UNSUPPORTED is returned.
+ *   - Inputs must be finite; non-finite inputs give unspecified (but in-bounds)
+ *     results.  Nothing is printed and nothing aborts.
+ *   - Calls on one stream are ordered; calls that share output or workspace
+ *     buffers on different streams race.  The library keeps no global state
+ *     other than a per-device cache of the architecture check.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1,
+  NVFP4_ERR_UNSUPPORTED = 2,
+  NVFP4_ERR_HIP = 3
+} nvfp4_status;
+
+typedef enum {
+  NVFP4_F32 = 0,  /* IEEE binary32 */
+  NVFP4_BF16 = 1  /* bfloat16; results are rounded to nearest even */
+} nvfp4_dtype;
+
+/* Version of this ABI (bumped on any incompatible change). */
+#define NVFP4_ABI_VERSION 1
+int nvfp4_abi_version(void);
+
+/* Static, human-readable name of a status code (host). */
+const char *nvfp4_status_string(nvfp4_status status);
+
+/* ------------------------------------------------------------------------
+ * Quantize (two-level scaling page: level 1 block scales, level 2 global
+ * scale; sub-section "The A4 side: dynamic activations").
+ *
+ * x       [rows][ld_x] of x_type (f32 or bf16), quantized along its first
+ *         `cols` columns; ld_x >= cols, in elements.
+ * rows    >= 0 (0 is a no-op apart from the global scale, see below)
+ * cols    > 0 and a multiple of 16
+ * q, s    outputs as described at the top of this file
+ * g       device float.  static_global == 0 (dynamic): written with
+ *         g = amax/2688 (amax = max|x|; 2688 = 6*448), or 1.0 when amax == 0.
+ *         static_global != 0: read as the caller's global scale (a positive
+ *         normal float >= 2^-100), not written.
+ * Per block (all float32, round to nearest even):
+ *   s = E4M3(min(bmax / (6*g), 448)), raised to 2^-9 if it rounds to 0;
+ *   r = 1 / (s*g);  code = E2M1(min(|x*r|, 6)) with the sign of x.
+ * workspace  device scratch of at least nvfp4_quantize_workspace_size(rows,
+ *         cols) bytes, 256-byte aligned (dynamic mode only; may be NULL when
+ *         the size is 0 or static_global != 0).  Its contents on entry do not
+ *         matter; it is clobbered.
+ * Precondition for the dynamic mode: amax == 0 or amax >= 2^-100.
+ * Alignment: x 16-byte aligned and ld_x*elem_size a multiple of 16 for the
+ * vectorised path; other layouts are accepted and take a slower path.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows,
+                            int64_t cols, int64_t ld_x, uint8_t *q, uint8_t *s,
+                            float *g, int static_global, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Batched dynamic quantize of `batch` independent matrices laid out
+ * contiguously: x [batch][rows][cols] (dense), q [batch][rows][cols/2],
+ * s [batch][rows][cols/16], g [batch]; matrix b gets its own global scale
+ * g[b] = amax_b/2688.  This is the offline (static) weight quantization of the
+ * per-expert matrices of an MoE (two-level scaling page, sub-section "The A4
+ * side": weights are quantized offline; one global scale per tensor).
+ * workspace: nvfp4_quantize_batched_workspace_size(batch, rows, cols) bytes. */
+size_t nvfp4_quantize_batched_workspace_size(int64_t batch, int64_t rows,
+                                             int64_t cols);
+nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type,
+                                    int64_t batch, int64_t rows, int64_t cols,
+                                    uint8_t *q, uint8_t *s, float *g,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dense W4A4 GEMM (Model-Optimizer QAD tutorial for Qwen3.6-35B-A3B, section
+ * "Why W4A4 rather than W4A16": both operands NVFP4, wide accumulation).
+ *
+ *   C[m][n] = a_g * b_g * sum_k e2m1(A[m][k]) e4m3(sA[m][k/16])
+ *                               * e2m1(B[n][k]) e4m3(sB[n][k/16])
+ * i.e. C = A_hat * B_hat^T with A [M x K] (activations) and B [N x K] (weights,
+ * one row per output feature), both NVFP4 along K.  Products of decoded
+ * operands are exact; accumulation is float32; the global scales are applied
+ * once in the epilogue; the result is rounded to c_type.
+ * M, N >= 0; K > 0 and a multiple of 16.  c is [M][ldc] of c_type, ldc >= N.
+ * a_g, b_g: device floats (read by the kernel; no host synchronization).
+ * Faster paths need K % 256 == 0 and 16-byte aligned q rows; other shapes are
+ * handled by a general path with the same results.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g,
+                        const uint8_t *b_q, const uint8_t *b_s, const float *b_g,
+                        int64_t M, int64_t N, int64_t K, void *c,
+                        nvfp4_dtype c_type, int64_t ldc, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MoE routing (two-level scaling page, section "Why only routed experts":
+ * each token uses k of E routed experts chosen by a BF16 router).
+ *
+ * logits  float [T][E] router logits.
+ * Top-k: the k largest logits per token, equal logits ordered by lower expert
+ * id; slot j holds the j-th largest.  topk_w = softmax over the k selected
+ * logits (float32).  Routed rows R = T*k are grouped by expert, then token:
+ *   expert_offsets int32 [E+1]  rows of expert e: [offsets[e], offsets[e+1])
+ *   src_row        int32 [T*k]  token of routed row r
+ *   inv            int32 [T][k] routed row of (token t, slot j)
+ *   topk_ids       int32 [T][k], topk_w float [T][k]
+ * 1 <= k <= E <= 1024, k <= 32, T >= 0, T*k < 2^31.
+ * workspace: nvfp4_moe_route_workspace_size(T, E, k) bytes (clobbered).
+ * The order is deterministic (a counting sort, no atomics).
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t E, int32_t k);
+nvfp4_status nvfp4_moe_route(const float *logits, int64_t T, int32_t E,
+                             int32_t k, int32_t *topk_ids, float *topk_w,
+                             int32_t *expert_offsets, int32_t *src_row,
+                             int32_t *inv, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped W4A4 GEMM over expert segments (two-level scaling page, section
+ * "Step 1: what NVFP4 touched": the routed experts' fused gate_up_proj and
+ * down_proj are the NVFP4 tensors).
+ *
+ * For every expert e and routed row r in [offsets[e], offsets[e+1]):
+ *   acc[r][n] = a_g * w_g[e] * sum_k A_hat[src(r)][k] * W_hat[e][n][k]
+ * where src(r) = src_row[r] if src_row != NULL (row gather fused into the
+ * operand load) else r.
+ * a_q/a_s/a_g  NVFP4 source activations [a_rows][K] (one global scale).
+ * expert_offsets  int32 [E+1] on the device, non-decreasing, offsets[0] = 0,
+ *              offsets[E] <= R (rows past offsets[E] are not written).
+ * R            host upper bound on offsets[E] (sizes the launch).
+ * w_q/w_s/w_g  expert weights [E][N][K/2], [E][N][K/16], [E].
+ * epilogue     NVFP4_EPI_NONE: c[r][n] = acc (c is [R][N] of c_type);
+ *              NVFP4_EPI_SILU_GATE: N = 2I, rows [0, I) of W are the gate and
+ *              [I, 2I) the up projection; c[r][i] = SiLU(acc[r][i]) *
+ *              acc[r][I+i] with SiLU(z) = z / (1 + exp(-z)), c is [R][I] of
+ *              c_type.
+ * K > 0, K % 16 == 0; N > 0 (even for SILU_GATE); E >= 1.
+ * ---------------------------------------------------------------------- */
+typedef enum { NVFP4_EPI_NONE = 0, NVFP4_EPI_SILU_GATE = 1 } nvfp4_epilogue;
+
+nvfp4_status nvfp4_moe_grouped_gemm(
+    const uint8_t *a_q, const uint8_t *a_s, const float *a_g, int64_t a_rows,
+    const int32_t *src_row, const int32_t *expert_offsets, int32_t E, int64_t R,
+    const uint8_t *w_q, const uint8_t *w_s, const float *w_g, int64_t N,
+    int64_t K, void *c, nvfp4_dtype c_type, nvfp4_epilogue epilogue,
+    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weighted unpermute (combine) of routed-row outputs back to tokens:
+ *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * y[inv[t][j]][h]
+ * summed in float32 in slot order, rounded to out_type.
+ * y [R][H] of y_type, topk_w float [T][k], inv int32 [T][k], out [T][H].
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_moe_combine(const void *y, nvfp4_dtype y_type,
+                               const float *topk_w, const int32_t *inv,
+                               int64_t T, int32_t k, int64_t H, int64_t R,
+                               void *out, nvfp4_dtype out_type,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

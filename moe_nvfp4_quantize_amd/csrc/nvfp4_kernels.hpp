@@ -1,0 +1,64 @@
+// nvfp4_kernels.hpp -- parameter blocks and launchers shared between the
+// kernels (*.hip) and the C ABI layer (api.cpp).  Internal; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_common.hpp"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------- quantize
+constexpr uint32_t kMaxPartials = 256;  // amax partials per matrix
+
+struct QuantParams {
+  const void *x;      // first element of matrix 0
+  int64_t ld;         // row stride of x, elements
+  int64_t x_mstride;  // elements between consecutive matrices
+  uint32_t rows, nbpr, units;  // nbpr = cols/16, units = rows*nbpr
+  FastDiv div_nbpr;
+  uint8_t *q;  // [batch][rows][cols/2]
+  uint8_t *s;  // [batch][rows][cols/16]
+  float *g;    // [batch]
+  int64_t q_mstride, s_mstride;  // bytes between matrices
+  float *partials;               // [batch][P] workspace
+  uint32_t P;                    // partials per matrix
+  int static_global;
+};
+
+uint32_t quantize_partials_per_matrix(uint64_t units);
+hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, hipStream_t stream);
+
+// -------------------------------------------------------------------- GEMM
+struct GemmParams {
+  const uint8_t *a_q, *a_s;
+  const float *a_g;
+  const uint8_t *b_q, *b_s;
+  const float *b_g;
+  uint32_t M, N, K;
+  void *c;
+  int64_t ldc;
+  // grouped (MoE) mode
+  const int32_t *src_row;         // nullable row gather
+  const int32_t *expert_offsets;  // [E+1]
+  uint32_t E;
+  int64_t b_mstride_q, b_mstride_s;  // bytes between expert matrices
+};
+
+enum class OutType { F32, BF16 };
+enum class Epilogue { None, SiluGate };
+
+hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epilogue epi,
+                               hipStream_t stream);
+
+// --------------------------------------------------------------------- MoE
+size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);
+hipError_t launch_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                        float *topk_w, int32_t *offsets, int32_t *src_row, int32_t *inv,
+                        void *workspace, hipStream_t stream);
+hipError_t launch_combine(const void *y, bool y_bf16, const float *w, const int32_t *inv, int64_t T,
+                          int32_t k, int64_t H, void *out, bool out_bf16, hipStream_t stream);
+
+}  // namespace nvfp4

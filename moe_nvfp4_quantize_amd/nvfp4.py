@@ -1,0 +1,267 @@
+"""Python binding of libnvfp4.so (C ABI in include/nvfp4.h).
+
+Argument marshalling only: every function here checks tensor placement and
+dtypes, allocates outputs and workspaces with torch when the caller did not pass
+them, and calls the C entry point of the same name on torch's current HIP
+stream.  All arithmetic runs in the library's HIP kernels; if the library is
+missing, the first call raises -- there is no fallback.
+
+Layouts follow the C header: an NVFP4 tensor is ``(q, s, g)`` with q uint8
+[rows, cols/2] (two E2M1 codes per byte, even element in the low nibble),
+s uint8 [rows, cols/16] (E4M3FN block scale codes) and g float32 [1] (the global
+decode scale), all on the GPU.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_ERR_INVALID_ARG, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_HIP = 0, 1, 2, 3
+NVFP4_F32, NVFP4_BF16 = 0, 1
+NVFP4_EPI_NONE, NVFP4_EPI_SILU_GATE = 0, 1
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); the order follows include/nvfp4.h
+SIGNATURES = {
+    "nvfp4_abi_version": (ctypes.c_int, []),
+    "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_quantize": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, ctypes.c_int,
+                                      _P, _SZ, _P]),
+    "nvfp4_quantize_batched_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_quantize_batched": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
+                                              _SZ, _P]),
+    "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _I64,
+                                  _P]),
+    "nvfp4_moe_route_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "nvfp4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_moe_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P,
+                                              _I64, _I64, _P, ctypes.c_int, ctypes.c_int, _P]),
+    "nvfp4_moe_combine": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _I64, _I32, _I64, _I64, _P,
+                                         ctypes.c_int, _P]),
+}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+def load_library(path=LIB_PATH):
+    """Load libnvfp4.so (once) and declare every exported signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m moe_nvfp4_quantize_amd.build` "
+            "(hipcc for gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().nvfp4_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != NVFP4_OK:
+        raise NVFP4Error(fn, status)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype_code(dtype):
+    if dtype == torch.float32:
+        return NVFP4_F32
+    if dtype == torch.bfloat16:
+        return NVFP4_BF16
+    raise TypeError(f"unsupported dtype {dtype}; float32 or bfloat16 expected")
+
+
+def _on_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ quantize
+
+
+def nvfp4_quantize(x, g=None, out=None, stream=None):
+    """Quantize a 2-D f32/bf16 GPU tensor along its last dim -> (q, s, g).
+
+    ``g=None``: dynamic global scale (amax/2688), written into the returned g.
+    ``g`` given (float32 [1] GPU tensor): static global scale, used as is.
+    ``out``: optional preallocated (q, s, g).
+    """
+    lib = load_library()
+    _on_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along the last dim")
+    rows, cols = x.shape
+    if out is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+        gg = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, s, gg = out
+    static = g is not None
+    if static:
+        gg.copy_(g.reshape(1))
+    ws_bytes = lib.nvfp4_quantize_workspace_size(rows, cols)
+    ws = _ws(ws_bytes, x.device)
+    st = lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
+                            _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(),
+                            _stream(stream))
+    _check("nvfp4_quantize", st)
+    return q, s, gg
+
+
+def nvfp4_quantize_batched(x, stream=None):
+    """Quantize each matrix of a contiguous [B, rows, cols] tensor with its own global scale."""
+    lib = load_library()
+    _on_gpu(x)
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 3-D tensor")
+    b, rows, cols = x.shape
+    q = torch.empty((b, rows, cols // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((b, rows, cols // 16), dtype=torch.uint8, device=x.device)
+    g = torch.empty(b, dtype=torch.float32, device=x.device)
+    ws = _ws(lib.nvfp4_quantize_batched_workspace_size(b, rows, cols), x.device)
+    st = lib.nvfp4_quantize_batched(_ptr(x), _dtype_code(x.dtype), b, rows, cols, _ptr(q), _ptr(s),
+                                    _ptr(g), _ptr(ws), ws.numel(), _stream(stream))
+    _check("nvfp4_quantize_batched", st)
+    return q, s, g
+
+
+# ---------------------------------------------------------------------- GEMM
+
+
+def nvfp4_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """C = A_hat @ B_hat^T for NVFP4 tensors a = (q, s, g) [M, K], b = (q, s, g) [N, K]."""
+    lib = load_library()
+    a_q, a_s, a_g = a
+    b_q, b_s, b_g = b
+    _on_gpu(a_q, a_s, a_g, b_q, b_s, b_g)
+    M, K = a_q.shape[0], a_q.shape[1] * 2
+    N = b_q.shape[0]
+    if b_q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between A and B")
+    for t in (a_q, a_s, b_q, b_s):
+        if not t.is_contiguous():
+            raise ValueError("q and s must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    st = lib.nvfp4_gemm(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(b_q), _ptr(b_s), _ptr(b_g), M, N, K,
+                        _ptr(out), _dtype_code(out.dtype), out.stride(0) if M else N,
+                        _stream(stream))
+    _check("nvfp4_gemm", st)
+    return out
+
+
+# ----------------------------------------------------------------------- MoE
+
+
+def nvfp4_moe_route(logits, k, stream=None):
+    """Top-k routing + permutation -> dict(topk_ids, topk_w, offsets, src_row, inv)."""
+    lib = load_library()
+    _on_gpu(logits)
+    if logits.dtype != torch.float32 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous float32")
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    src_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = _ws(lib.nvfp4_moe_route_workspace_size(T, E, k), dev)
+    st = lib.nvfp4_moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(offsets),
+                             _ptr(src_row), _ptr(inv), _ptr(ws), ws.numel(), _stream(stream))
+    _check("nvfp4_moe_route", st)
+    return dict(topk_ids=ids, topk_w=w, offsets=offsets, src_row=src_row, inv=inv)
+
+
+def nvfp4_moe_grouped_gemm(a, src_row, offsets, R, w, epilogue=NVFP4_EPI_NONE,
+                           out_dtype=torch.float32, out=None, stream=None):
+    """Grouped GEMM over expert segments; a = (q, s, g) source rows, w = stacked expert weights."""
+    lib = load_library()
+    a_q, a_s, a_g = a
+    w_q, w_s, w_g = w
+    _on_gpu(a_q, a_s, a_g, src_row, offsets, w_q, w_s, w_g)
+    E, N, khalf = w_q.shape
+    K = khalf * 2
+    if a_q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and expert weights")
+    n_out = N // 2 if epilogue == NVFP4_EPI_SILU_GATE else N
+    if out is None:
+        out = torch.empty((R, n_out), dtype=out_dtype, device=a_q.device)
+    st = lib.nvfp4_moe_grouped_gemm(_ptr(a_q), _ptr(a_s), _ptr(a_g), a_q.shape[0], _ptr(src_row),
+                                    _ptr(offsets), E, R, _ptr(w_q), _ptr(w_s), _ptr(w_g), N, K,
+                                    _ptr(out), _dtype_code(out.dtype), epilogue, _stream(stream))
+    _check("nvfp4_moe_grouped_gemm", st)
+    return out
+
+
+def nvfp4_moe_combine(y, topk_w, inv, out_dtype=torch.bfloat16, out=None, stream=None):
+    """out[t] = sum_j topk_w[t, j] * y[inv[t, j]]."""
+    lib = load_library()
+    _on_gpu(y, topk_w, inv)
+    T, k = inv.shape
+    R, H = y.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y.device)
+    st = lib.nvfp4_moe_combine(_ptr(y), _dtype_code(y.dtype), _ptr(topk_w), _ptr(inv), T, k, H, R,
+                               _ptr(out), _dtype_code(out.dtype), _stream(stream))
+    _check("nvfp4_moe_combine", st)
+    return out
+
+
+def moe_layer(x, logits, k, w_gate_up, w_down, stream=None, keep=False):
+    """The routed-expert layer as a sequence of library calls.
+
+    x bf16/f32 [T, H]; w_gate_up and w_down are quantized expert stacks
+    (q, s, g) for [E, 2I, H] and [E, H, I].  Returns the bf16 output, or with
+    ``keep=True`` a dict of every intermediate.
+    """
+    T = x.shape[0]
+    r = nvfp4_moe_route(logits, k, stream=stream)
+    R = T * k
+    xq = nvfp4_quantize(x, stream=stream)
+    h = nvfp4_moe_grouped_gemm(xq, r["src_row"], r["offsets"], R, w_gate_up,
+                               epilogue=NVFP4_EPI_SILU_GATE, out_dtype=torch.float32, stream=stream)
+    hq = nvfp4_quantize(h, stream=stream)
+    y = nvfp4_moe_grouped_gemm(hq, None, r["offsets"], R, w_down, out_dtype=torch.float32,
+                               stream=stream)
+    out = nvfp4_moe_combine(y, r["topk_w"], r["inv"], stream=stream)
+    if keep:
+        return dict(r, xq=xq, h=h, hq=hq, y=y, out=out)
+    return out

@@ -1,0 +1,162 @@
+"""GPU parity of nvfp4_quantize / nvfp4_quantize_batched against the oracle.
+
+Bar: q, s and g bit-exact.  Full tensors where the oracle finishes in seconds;
+at the full workload sizes, the global scale is checked in full and the codes
+and scales of sampled rows (the oracle quantizes any row given g).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4 as Q
+from moe_nvfp4_quantize_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from moe_nvfp4_quantize_amd import nvfp4
+    nvfp4.load_library()
+    return nvfp4
+
+
+def _host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _check_full(B, x, g_static=None):
+    print(f"[quantize] shape={tuple(x.shape)} dtype={x.dtype} static={g_static is not None}", flush=True)
+    g_in = None if g_static is None else torch.tensor([g_static], dtype=torch.float32, device=x.device)
+    q, s, g = B.nvfp4_quantize(x, g=g_in)
+    torch.cuda.synchronize()
+    rq, rs, rg = Q.quantize(_host(x), g=g_static)
+    assert g.item() == rg
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def test_linear_16x512_x_and_w(B):
+    x, w = W.linear_inputs("linear_16x512", device="cuda")
+    _check_full(B, x)
+    _check_full(B, w)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (7, 4096 + 16), (129, 272), (1000, 32)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_shapes(B, rows, cols, dtype):
+    x = W.random_matrix(rows, cols, seed=rows * 7 + cols, dtype=dtype, device="cuda", std=3.0)
+    _check_full(B, x)
+
+
+def test_strided_rows_take_the_unaligned_path(B):
+    base = W.random_matrix(33, 96 + 3, seed=4, dtype=torch.bfloat16, device="cuda")
+    x = base[:, :96]  # row stride 99 elements: not 16-byte aligned
+    q, s, g = B.nvfp4_quantize(x)
+    rq, rs, rg = Q.quantize(_host(x))
+    assert g.item() == rg
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def test_degenerate_values(B):
+    z = torch.zeros((4, 64), device="cuda")
+    _check_full(B, z)
+    _check_full(B, -z)  # negative zero keeps its sign bit: codes 0x8
+    one_hot = torch.zeros((2, 48), device="cuda")
+    one_hot[1, 20] = -3.0
+    _check_full(B, one_hot)
+    tiny = W.random_matrix(8, 64, seed=5, device="cuda") * 1e-25
+    _check_full(B, tiny)
+    huge = W.random_matrix(8, 64, seed=6, device="cuda") * 1e30
+    _check_full(B, huge)
+    # exact E2M1 midpoints after scaling: amax 2688 -> g = 1, block scale 448
+    mids = torch.tensor([[2688.0] + [448.0 * m for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] * 2
+                         + [0.0] * 1], device="cuda")
+    _check_full(B, mids[:, :16])
+
+
+def test_representable_round_trip(B):
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 16, size=(64, 256)).astype(np.uint8)
+    codes[:, ::16] = 7
+    s = rng.integers(1, 127, size=(64, 16)).astype(np.uint8)
+    s[0, 0] = 0x7E
+    from oracle.formats import e2m1_decode, e4m3_decode
+    x = (e2m1_decode(codes).reshape(64, 16, 16) * e4m3_decode(s)[..., None]).reshape(64, 256) * 2.0 ** -6
+    xt = torch.from_numpy(x.astype(np.float32)).cuda()
+    q, sg, g = B.nvfp4_quantize(xt)
+    assert g.item() == 2.0 ** -6
+    np.testing.assert_array_equal(sg.cpu().numpy(), s)
+    np.testing.assert_array_equal(q.cpu().numpy(), Q.pack_codes(codes))
+
+
+def test_static_global_scale(B):
+    x, _ = W.linear_inputs("linear_16x512", device="cuda")
+    g = Q.global_scale(_host(x))
+    _check_full(B, x, g_static=float(g))
+    _check_full(B, x, g_static=float(np.float32(g) / np.float32(64)))  # saturating
+    _check_full(B, x, g_static=float(np.float32(g) * np.float32(1000)))  # tiny scales
+
+
+def test_empty_tensor_dynamic_gives_unit_global(B):
+    x = torch.zeros((0, 64), device="cuda")
+    q, s, g = B.nvfp4_quantize(x)
+    assert g.item() == 1.0 and q.numel() == 0
+
+
+def _sampled(B, x, rows):
+    q, s, g = B.nvfp4_quantize(x)
+    torch.cuda.synchronize()
+    rg = Q.global_scale(_host(x))
+    assert g.item() == rg
+    xs = _host(x[rows])
+    rq, rs, _ = Q.quantize(xs, g=rg)
+    np.testing.assert_array_equal(s[rows].cpu().numpy(), rs)
+    np.testing.assert_array_equal(q[rows].cpu().numpy(), rq)
+    # properties over the whole tensor: scales positive finite, max 448 exactly
+    sh = s.cpu().numpy()
+    assert sh.max() == 0x7E and sh.min() >= 1 and np.all((sh & 0x7F) != 0x7F)
+    return q, s, g
+
+
+def test_prefill_8192x5120_activation_sampled(B):
+    x, _ = W.linear_inputs("prefill_8192x5120", device="cuda")
+    print("[quantize] prefill X 8192x5120 bf16", flush=True)
+    rows = torch.tensor([0, 1, 2, 777, 4095, 4096, 8190, 8191] + list(range(100, 8192, 331)), device="cuda")
+    _sampled(B, x, rows)
+
+
+def test_prefill_8192x5120_weight_sampled(B):
+    _, w = W.linear_inputs("prefill_8192x5120", device="cuda", M=1)
+    print("[quantize] prefill W 25600x5120 bf16", flush=True)
+    rows = torch.tensor([0, 1, 12799, 12800, 25599] + list(range(7, 25600, 997)), device="cuda")
+    _sampled(B, w, rows)
+
+
+def test_lmhead_weight_sampled(B):
+    _, w = W.linear_inputs("lmhead_128x151936", device="cuda", M=1)
+    print("[quantize] lm_head W 151936x2048 bf16", flush=True)
+    rows = torch.tensor([0, 151935] + list(range(3, 151936, 4999)), device="cuda")
+    _sampled(B, w, rows)
+
+
+def test_batched_matches_per_matrix(B):
+    x = W.random_matrix(5 * 48, 96, seed=8, dtype=torch.bfloat16, device="cuda").reshape(5, 48, 96)
+    x[2] *= 100.0
+    x[4] = 0.0
+    q, s, g = B.nvfp4_quantize_batched(x.contiguous())
+    for b in range(5):
+        rq, rs, rg = Q.quantize(_host(x[b]))
+        assert g[b].item() == rg, b
+        np.testing.assert_array_equal(s[b].cpu().numpy(), rs)
+        np.testing.assert_array_equal(q[b].cpu().numpy(), rq)
+
+
+def test_deterministic(B):
+    x, _ = W.linear_inputs("prefill_8192x5120", device="cuda", M=512)
+    a = B.nvfp4_quantize(x)
+    b = B.nvfp4_quantize(x)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
