@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the layer over one batch of synthetic, seeded input that is
+already resident in HBM:
+  dense workloads  : dynamic NVFP4 quantize of the activations (amax pass +
+                     encode pass) followed by the W4A4 GEMM against weights
+                     quantized once, offline (static), before timing;
+  MoE workloads    : router top-k + softmax + permutation, activation quantize,
+                     grouped gate_up GEMM with fused SiLU gate, quantize of h,
+                     grouped down GEMM, weighted combine.
+The default workload is the dense prefill up-projection X[8192x5120] W[25600x5120]
+(bf16 in, bf16 out).  ``value`` is the step's effective rate 2*M*N*K / step time
+in TFLOP/s; the activation quantizer's HBM rate (GB/s) and each kernel's share of
+its roofline are reported beside it.  Kernel durations come from HIP events
+recorded on the stream the kernels run on, around each kernel inside the timed
+region.
+
+Prints ONE JSON line (see the keys below).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from moe_nvfp4_quantize_amd import workloads as W  # noqa: E402
+
+METRIC = "NVFP4 GEMM eff. TFLOPS & quantize GB/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA, TFLOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense FP4, context only
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill_8192x5120", choices=sorted(W.WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def quant_bytes(numel, in_bytes):
+    """Algorithmic HBM bytes of one quantize: read x, write codes (0.5 B) and scales (1/16 B)."""
+    return numel * (in_bytes + 0.5 + 1.0 / 16.0)
+
+
+class Timer:
+    """Pairs of HIP events on the current stream, averaged over the timed steps."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ev = {n: [] for n in names}
+
+    def mark(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, name, start, end):
+        self.ev[name].append((start, end))
+
+    def mean_ms(self, name):
+        pairs = self.ev[name]
+        return sum(a.elapsed_time(b) for a, b in pairs) / max(1, len(pairs))
+
+
+# ----------------------------------------------------------------- dense
+
+
+def setup_dense(B, name):
+    cfg = W.WORKLOADS[name]
+    x, w = W.linear_inputs(name, device="cuda")
+    wq = B.nvfp4_quantize(w)  # offline static weights, untimed
+    del w
+    xq = (torch.empty((cfg["M"], cfg["K"] // 2), dtype=torch.uint8, device="cuda"),
+          torch.empty((cfg["M"], cfg["K"] // 16), dtype=torch.uint8, device="cuda"),
+          torch.empty(1, dtype=torch.float32, device="cuda"))
+    out_dtype = torch.bfloat16 if cfg["out"] == "bf16" else torch.float32
+    y = torch.empty((cfg["M"], cfg["N"]), dtype=out_dtype, device="cuda")
+    return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y)
+
+
+def step_dense(B, st, timer=None):
+    t0 = timer.mark() if timer else None
+    B.nvfp4_quantize(st["x"], out=st["xq"])
+    t1 = timer.mark() if timer else None
+    B.nvfp4_gemm(st["xq"], st["wq"], out=st["y"])
+    if timer:
+        t2 = timer.mark()
+        timer.add("quantize", t0, t1)
+        timer.add("gemm", t1, t2)
+
+
+def report_dense(st, timer, step_ms):
+    cfg = st["cfg"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    flops = 2.0 * M * N * K
+    gemm_ms = timer.mean_ms("gemm")
+    q_ms = timer.mean_ms("quantize")
+    in_b = 2 if cfg["x_dtype"] == "bf16" else 4
+    out_b = 2 if cfg["out"] == "bf16" else 4
+    qbytes = quant_bytes(M * K, in_b)
+    gemm_bytes = 0.5625 * (M * K + N * K) + out_b * M * N
+    t_mfma = flops / (F16_MFMA_PEAK_TFLOPS * 1e12)
+    t_hbm = gemm_bytes / (HBM_PEAK_GBS * 1e9)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    gemm_gbs = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    if t_mfma >= t_hbm:
+        roof = dict(bound="mfma", achieved=gemm_tflops, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=gemm_tflops / F16_MFMA_PEAK_TFLOPS)
+    else:
+        roof = dict(bound="hbm", achieved=gemm_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=gemm_gbs / HBM_PEAK_GBS)
+    roof.update(kernel="nvfp4 gemm_kernel", traffic=None,
+                per_launch=dict(flops=flops, algorithmic_bytes=gemm_bytes, avg_ms=gemm_ms))
+    q_gbs = qbytes / (q_ms * 1e-3) / 1e9
+    extra = dict(
+        gemm=dict(avg_ms=gemm_ms, tflops=gemm_tflops, frac_f16_peak=gemm_tflops / F16_MFMA_PEAK_TFLOPS,
+                  frac_fp4_peak=gemm_tflops / FP4_MFMA_PEAK_TFLOPS, gbs=gemm_gbs),
+        quantize=dict(avg_ms=q_ms, gbs=q_gbs, frac_hbm=q_gbs / HBM_PEAK_GBS,
+                      algorithmic_bytes=qbytes, kernels="amax_partials + quantize"),
+    )
+    value = flops / (step_ms * 1e-3) / 1e12
+    config = dict(workload=st["name"], M=M, N=N, K=K, x=cfg["x_dtype"], out=cfg["out"],
+                  weights="NVFP4, quantized offline (static)", activations="NVFP4, dynamic, quantized in the step")
+    return value, "TFLOP/s", roof, extra, config
+
+
+# ------------------------------------------------------------------- MoE
+
+
+def setup_moe(B, name):
+    cfg = W.WORKLOADS[name]
+    inp = W.moe_inputs(name, device="cuda")
+    wgu = B.nvfp4_quantize_batched(inp["w_gate_up"])
+    wd = B.nvfp4_quantize_batched(inp["w_down"])
+    del inp["w_gate_up"], inp["w_down"]
+    return dict(cfg=cfg, name=name, x=inp["x"], logits=inp["logits"], k=inp["k"], wgu=wgu, wd=wd)
+
+
+def step_moe(B, st, timer=None):
+    T = st["x"].shape[0]
+    k = st["k"]
+    R = T * k
+    m = [timer.mark()] if timer else None
+    r = B.nvfp4_moe_route(st["logits"], k)
+    if timer: m.append(timer.mark())
+    xq = B.nvfp4_quantize(st["x"])
+    if timer: m.append(timer.mark())
+    h = B.nvfp4_moe_grouped_gemm(xq, r["src_row"], r["offsets"], R, st["wgu"],
+                                 epilogue=B.NVFP4_EPI_SILU_GATE, out_dtype=torch.float32)
+    if timer: m.append(timer.mark())
+    hq = B.nvfp4_quantize(h)
+    if timer: m.append(timer.mark())
+    y = B.nvfp4_moe_grouped_gemm(hq, None, r["offsets"], R, st["wd"], out_dtype=torch.float32)
+    if timer: m.append(timer.mark())
+    B.nvfp4_moe_combine(y, r["topk_w"], r["inv"])
+    if timer:
+        m.append(timer.mark())
+        for i, n in enumerate(["route", "quantize_x", "gate_up", "quantize_h", "down", "combine"]):
+            timer.add(n, m[i], m[i + 1])
+
+
+def report_moe(st, timer, step_ms):
+    cfg = st["cfg"]
+    T, E, k, H, I = cfg["T"], cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+    R = T * k
+    f_gu = 2.0 * R * 2 * I * H
+    f_d = 2.0 * R * H * I
+    flops = f_gu + f_d
+    gu_ms = timer.mean_ms("gate_up")
+    gu_tflops = f_gu / (gu_ms * 1e-3) / 1e12
+    roof = dict(bound="mfma", achieved=gu_tflops, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel="nvfp4 gemm_kernel (grouped, SiLU gate)",
+                traffic=None, per_launch=dict(flops=f_gu, avg_ms=gu_ms))
+    parts = {n: timer.mean_ms(n) for n in timer.names}
+    d_ms = parts["down"]
+    qh_bytes = quant_bytes(R * I, 4)
+    extra = dict(stages_ms=parts, down=dict(tflops=f_d / (d_ms * 1e-3) / 1e12),
+                 quantize_h=dict(gbs=qh_bytes / (parts["quantize_h"] * 1e-3) / 1e9))
+    value = flops / (step_ms * 1e-3) / 1e12
+    config = dict(workload=st["name"], T=T, E=E, k=k, H=H, I=I, x="bf16", out="bf16",
+                  experts="NVFP4 gate_up [2I x H] and down [H x I], quantized offline")
+    return value, "TFLOP/s", roof, extra, config
+
+
+# ----------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline_dense(cfg_name):
+    """The oracle on a bounded sample of the dense step, extrapolated to the full step."""
+    import numpy as np
+    from oracle import gemm as OG
+    from oracle import nvfp4 as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    cfg = W.WORKLOADS[cfg_name]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    mq, mg, ng = min(M, 256), min(M, 64), min(N, 2560)
+    x, w = W.linear_inputs(cfg_name, device="cpu")
+    xh = x.float().numpy()
+    wh = w[:ng].float().numpy()
+    gw = OQ.global_scale(w.float().numpy())
+    wq = OQ.quantize(wh, g=gw)  # offline weights: not timed
+    t0 = time.perf_counter()
+    gx = OQ.global_scale(xh)
+    OQ.quantize(xh[:mq], g=gx)
+    tq = time.perf_counter() - t0
+    xq = OQ.quantize(xh[:mg], g=gx)
+    t0 = time.perf_counter()
+    OG.gemm(*xq, *wq)
+    tg = time.perf_counter() - t0
+    step_s = tq * (M / mq) + tg * (M * N) / (mg * ng)
+    return dict(value=2.0 * M * N * K / step_s / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"quantize {mq} of {M} activation rows (global scale over all rows) and GEMM "
+                       f"{mg}x{ng} of {M}x{N} outputs (K={K}), float64 numpy; times scaled by the "
+                       f"row/output counts to one full step ({step_s:.1f} s)")
+
+
+def cpu_baseline_moe(cfg_name):
+    return None
+
+
+# ------------------------------------------------------------------- main
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    from moe_nvfp4_quantize_amd import nvfp4 as B
+    B.load_library()
+    torch.cuda.set_device(0)
+    kind = W.WORKLOADS[args.workload]["kind"]
+    if kind == "linear":
+        st, step, report = setup_dense(B, args.workload), step_dense, report_dense
+        names = ["quantize", "gemm"]
+    else:
+        st, step, report = setup_moe(B, args.workload), step_moe, report_moe
+        names = ["route", "quantize_x", "gate_up", "quantize_h", "down", "combine"]
+
+    for _ in range(args.warmup):
+        step(B, st)
+    torch.cuda.synchronize()
+
+    # whole-step wall time: K steps between two synchronizations
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(B, st)
+    t_end.record()
+    torch.cuda.synchronize()
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel durations: the same steps again with events around every kernel
+    timer = Timer(names)
+    for _ in range(args.steps):
+        step(B, st, timer)
+    torch.cuda.synchronize()
+
+    if args.copy_probe_mib:
+        a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    value, unit, roof, extra, config = report(st, timer, step_ms)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_dense(args.workload) if kind == "linear" else cpu_baseline_moe(args.workload)
+    line = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=step_ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="f16", data="synthetic", config=config, roofline=roof, cpu_baseline=cpu,
+                **extra)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
