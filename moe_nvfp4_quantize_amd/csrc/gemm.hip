@@ -10,20 +10,32 @@
 //    elements; NVFP4 has an E4M3 scale (3 mantissa bits) per 16.  A product
 //    e2m1 * e4m3 has at most 6 significant bits and lies in [2^-10, 2688], so
 //    it is exact in f16.  Each operand is therefore decoded in registers to f16
-//    (hardware FP4->f16 convert, then one packed multiply by the block scale)
-//    and fed to v_mfma_f32_32x32x16_f16 with float32 accumulation.  The global
+//    and fed to v_mfma_f32_32x32x16_f16 with float32 accumulation; the global
 //    scales are applied once, in the epilogue.
+//  * Decode of 8 codes (one dword) with block scale s: four hardware FP4->f16
+//    converts with unit scale (the convert's own scale operand only applies a
+//    power of two, so it cannot carry an E4M3 scale) and four packed f16
+//    multiplies by (s, s).  The f16 form of s comes from bits: an E4M3FN byte c
+//    shifted left by 7 is an f16 whose value is s * 2^-8 (normal and subnormal
+//    alike), and one packed multiply by 256 makes it s.
 //  * Packed operands stay packed until the last moment: global -> LDS moves
-//    0.5625 B per element (codes + scales), so LDS traffic is a quarter of a
-//    f16 GEMM's and the tile loads are 128-byte row segments.
-//  * K order inside a 256-wide K step is permuted identically for both
+//    0.5625 B per element (codes + scales), a quarter of an f16 GEMM's LDS
+//    traffic; LDS is double buffered and the next K step's global loads are in
+//    flight while the current one is multiplied.
+//  * Large wave tiles (up to 128 x 128 per wave) amortise each decoded
+//    fragment over 4 MFMAs in each direction: the decode work per MFMA falls as
+//    1/WM + 1/WN.
+//  * K order inside a 128-wide K step is permuted identically for both
 //    operands (a GEMM sums over K, so any common order is exact): lane half h of
-//    a wave owns packed bytes [64h, 64h + 64) of each row (K elements
-//    [128h, 128h + 128)), and MFMA step t consumes its dword t.  One lane then
-//    reads its 64 bytes with four 16-byte LDS loads and one 16-byte load of
-//    its eight f16 block scales.
-//  * LDS rows are padded to 144 bytes so that the 16-byte reads of 8
+//    a wave owns packed bytes [32h, 32h + 32) of each row (K elements
+//    [64h, 64h + 64), blocks 4h..4h+3), and MFMA step t consumes its dword t.
+//  * LDS rows of codes are padded to 80 bytes so the 16-byte reads of 8
 //    consecutive rows fall in distinct banks.
+//  * The epilogue stages each wave's 32-row slab through LDS so that global
+//    stores are 16 bytes per lane along a row.
+//  * Dense tiles are ordered XCD-aware: workgroup w runs on XCD w % 8, so each
+//    XCD is given a contiguous range of tiles, swept 8 tile-rows at a time so
+//    that concurrently running workgroups share A and B tiles in that XCD's L2.
 #include "nvfp4_common.hpp"
 #include "nvfp4_format.hpp"
 #include "nvfp4_kernels.hpp"
@@ -36,90 +48,114 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 256;          // K elements per main-loop step
-constexpr int KB = BK / 2;       // packed bytes per row per step
-constexpr int SB = BK / 16;      // scales per row per step
-constexpr int ROWB = KB + 16;    // padded LDS row of packed codes, bytes
-constexpr int SROWH = SB;        // LDS row of f16 scales, halves
+constexpr int BK = 128;        // K elements per stage
+constexpr int KB = BK / 2;     // packed bytes per row per stage
+constexpr int SBY = BK / 16;   // scale bytes per row per stage
+constexpr int ROWB = KB + 16;  // padded LDS row of codes, bytes
 
-// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times one
-// f16 block scale -> 8 exact f16 products.
+template <int BM, int BN, int WM, int WN>
+struct Tile {
+  static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int CHA = BM * 4 / NT, CHB = BN * 4 / NT;  // 16-byte code chunks per thread
+  static constexpr int OFF_B = BM * ROWB;
+  static constexpr int OFF_SA = OFF_B + BN * ROWB;
+  static constexpr int OFF_SB = OFF_SA + BM * SBY;
+  static constexpr int STAGE = OFF_SB + BN * SBY;
+  static_assert(BM * 4 % NT == 0 && BN * 4 % NT == 0, "code chunks must split evenly");
+};
+
+// two E4M3FN scale bytes (bits 7..0 and 23..16 of w) -> f16 pair (exact)
+__device__ __forceinline__ half2v scale_pair(uint32_t w) {
+  const uint32_t bits = (w & 0x00FF00FFu) << 7;
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(half2v, bits) * k256;
+}
+
+// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times the
+// f16 block scale s -> 8 exact f16 products
 __device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
   const half2v s2 = {s, s};
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
-  half8v r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// E4M3 scale byte -> f16 (exact: E4M3FN values lie in [2^-9, 448]).
-__device__ __forceinline__ _Float16 scale_f16(uint32_t code) {
-  return code ? (_Float16)e4m3_value(code & 0x7Fu) : (_Float16)0.0f;
-}
-
-template <typename OutT>
-__device__ __forceinline__ void store_out(OutT *p, float v);
-template <>
-__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
-template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) {
-  *p = (uint16_t)float_to_bf16_bits(v);
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return (half8v){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// One workgroup computes a BM x BN output tile with (BM/WM) x (BN/WN) waves,
-// each owning WM x WN as (WM/32) x (WN/32) MFMA 32x32 tiles.
-//  GROUPED: the M tiles walk the expert segments given by expert_offsets; rows
-//           may be gathered through src_row; B is the expert's matrix.
-//  ALIGNED: K % 256 == 0 and all operand rows 16-byte aligned.
-//  SILU:    (GROUPED only, WN == 64) B-tile columns are gate/up pairs and the
-//           output is SiLU(gate) * up with N/2 columns.
-template <int BM, int BN, int WM, int WN, bool GROUPED, bool ALIGNED, bool SILU, typename OutT>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmParams p) {
-  constexpr int NW_N = BN / WN;
-  constexpr int NT = (BM / WM) * NW_N * 64;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(!SILU || FN == 2, "SiLU pairing needs two 32-column fragments per wave");
+template <typename OutT>
+__device__ __forceinline__ OutT to_out(float v);
+template <>
+__device__ __forceinline__ float to_out<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return (uint16_t)float_to_bf16_bits(v); }
 
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BN * ROWB];
-  __shared__ __attribute__((aligned(16))) _Float16 sAs[BM * SROWH];
-  __shared__ __attribute__((aligned(16))) _Float16 sBs[BN * SROWH];
+// Which tile a dense workgroup computes (see the XCD note at the top).
+__device__ __forceinline__ void dense_tile(uint32_t w, uint32_t tiles_m, uint32_t tiles_n,
+                                           uint32_t *tm, uint32_t *tn) {
+  const uint32_t G = tiles_m * tiles_n;
+  const uint32_t q = G / 8, r = G % 8, x = w % 8, local = w / 8;
+  const uint32_t idx = x * q + min(x, r) + local;
+  constexpr uint32_t GM = 8;
+  const uint32_t group = idx / (GM * tiles_n);
+  const uint32_t first_m = group * GM;
+  const uint32_t gsize = min(tiles_m - first_m, GM);
+  const uint32_t pid = idx - group * GM * tiles_n;
+  *tm = first_m + pid % gsize;
+  *tn = pid / gsize;
+}
+
+// One workgroup computes a BM x BN tile of acc with NWM x NWN waves, each
+// owning WM x WN as FM x FN MFMA 32x32 tiles.
+//  GROUPED: M tiles walk the expert segments given by expert_offsets; rows may
+//           be gathered through src_row; B is the expert's matrix.
+//  ALIGNED: K % 128 == 0 and q/s bases 16/8-byte aligned: vector loads.
+//  SILU:    (GROUPED only) in every wave the first FN/2 fragments hold gate
+//           columns and the last FN/2 the matching up columns; the output is
+//           SiLU(gate) * up with N/2 columns.
+//  VSTORE:  output rows are 16-byte aligned: 16-byte stores.
+template <int BM, int BN, int WM, int WN, bool GROUPED, bool ALIGNED, bool SILU, bool VSTORE,
+          typename OutT>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(GemmParams p) {
+  using TL = Tile<BM, BN, WM, WN>;
+  constexpr int NT = TL::NT, FM = TL::FM, FN = TL::FN, NWN = TL::NWN;
+  constexpr int HALF = FN / 2;
+  static_assert(!SILU || FN % 2 == 0, "SiLU pairing needs an even number of column fragments");
+  constexpr uint32_t BN_OUT = SILU ? BN / 2 : BN;
+  constexpr int WN_OUT = SILU ? WN / 2 : WN;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TL::STAGE];
   __shared__ int32_t sRow[BM];  // source row of each tile row, -1 past the end
-  __shared__ int32_t sInfo[2];  // grouped: expert, first routed row of the tile
+  __shared__ int32_t sInfo[2];
 
   const uint32_t tid = threadIdx.x;
   const uint32_t K = p.K;
   const uint32_t kbytes = K / 2, kscales = K / 16;
-  const uint32_t n_out = SILU ? p.N / 2 : p.N;  // output columns
-  constexpr uint32_t BN_OUT = SILU ? BN / 2 : BN;
+  const uint32_t n_out = SILU ? p.N / 2 : p.N;
   const uint32_t tiles_n = (n_out + BN_OUT - 1) / BN_OUT;
 
-  // ---- which tile
+  // ---------------------------------------------------------------- tile
   uint32_t tile_n, row0, row_end;
   const uint8_t *bq = p.b_q;
   const uint8_t *bs = p.b_s;
   float b_g;
   if (!GROUPED) {
     const uint32_t tiles_m = (p.M + BM - 1) / BM;
-    const uint32_t bid = blockIdx.x;
-    tile_n = bid / tiles_m;
-    row0 = (bid - tile_n * tiles_m) * BM;
+    uint32_t tm;
+    dense_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tile_n);
+    row0 = tm * BM;
     row_end = p.M;
     b_g = *p.b_g;
   } else {
-    // tile_mm-th M tile over all experts, each expert contributing ceil(n_e/BM)
+    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM)
     tile_n = blockIdx.x % tiles_n;
     const uint32_t tile_mm = blockIdx.x / tiles_n;
-    if (tid == 0) { sInfo[0] = -1; sInfo[1] = 0; }
-    __syncthreads();
-    // serial scan in chunks of NT experts: thread t owns expert c*NT + t
+    __shared__ uint32_t scan[NT];
+    if (tid == 0) sInfo[0] = -1;
     uint32_t base = 0;
     for (uint32_t c0 = 0; c0 < p.E; c0 += NT) {
       const uint32_t e = c0 + tid;
@@ -128,12 +164,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmPa
         lo = (uint32_t)p.expert_offsets[e];
         cnt = ((uint32_t)p.expert_offsets[e + 1] - lo + BM - 1) / BM;
       }
-      // inclusive prefix over the chunk through LDS
-      __shared__ uint32_t scan[NT];
       scan[tid] = cnt;
       __syncthreads();
       for (uint32_t off = 1; off < NT; off <<= 1) {
-        uint32_t v = tid >= off ? scan[tid - off] : 0;
+        const uint32_t v = tid >= off ? scan[tid - off] : 0;
         __syncthreads();
         scan[tid] += v;
         __syncthreads();
@@ -147,7 +181,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmPa
       base += scan[NT - 1];
       __syncthreads();
     }
-    if (sInfo[0] < 0) return;  // past the last tile (uniform across the workgroup)
+    if (sInfo[0] < 0) return;  // past the last tile: the whole workgroup leaves
     const uint32_t e = (uint32_t)sInfo[0];
     row0 = (uint32_t)sInfo[1];
     row_end = (uint32_t)p.expert_offsets[e + 1];
@@ -163,24 +197,97 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmPa
     if (row < row_end) src = (GROUPED && p.src_row) ? p.src_row[row] : (int32_t)row;
     sRow[r] = src;
   }
-  // B-tile row rho -> weight row
+  // B-tile row rho -> weight row (or -1 past N)
   auto b_row = [&](uint32_t rho) -> int32_t {
-    uint32_t n;
     if (SILU) {
       const uint32_t half = p.N / 2;
-      const uint32_t col = tile_n * BN_OUT + (rho / 64) * 32 + (rho % 32);
+      const uint32_t wn = rho / WN, j = (rho % WN) / 32, c = rho % 32;
+      const uint32_t col = tile_n * BN_OUT + wn * (WN / 2) + (j % HALF) * 32 + c;
       if (col >= half) return -1;
-      n = ((rho % 64) < 32) ? col : half + col;
-    } else {
-      n = tile_n * BN + rho;
-      if (n >= p.N) return -1;
+      return (int32_t)(j < (uint32_t)HALF ? col : half + col);
     }
-    return (int32_t)n;
+    const uint32_t n = tile_n * BN + rho;
+    return n < p.N ? (int32_t)n : -1;
   };
   __syncthreads();
 
+  // per-thread source rows of the code chunks it loads (fixed over K)
+  int32_t srcA[TL::CHA], srcB[TL::CHB];
+#pragma unroll
+  for (int i = 0; i < TL::CHA; ++i) srcA[i] = sRow[(tid + i * NT) / 4];
+#pragma unroll
+  for (int i = 0; i < TL::CHB; ++i) srcB[i] = b_row((tid + i * NT) / 4);
+  constexpr int SCH = (BM + BN + NT - 1) / NT;  // scale rows per thread
+  int32_t srcS[SCH];
+#pragma unroll
+  for (int i = 0; i < SCH; ++i) {
+    const uint32_t c = tid + i * NT;
+    srcS[i] = c < (uint32_t)BM ? sRow[c] : (c < (uint32_t)(BM + BN) ? b_row(c - BM) : -1);
+  }
+
+  u32x4 ra[TL::CHA], rb[TL::CHB];
+  u32x2 rs[SCH];
+  auto load_global = [&](uint32_t ks) {
+    const uint32_t kb0 = ks * KB, ksc0 = ks * SBY;
+#pragma unroll
+    for (int i = 0; i < TL::CHA + TL::CHB; ++i) {
+      const bool isA = i < TL::CHA;
+      const uint32_t c = tid + (isA ? i : i - TL::CHA) * NT;
+      const int32_t src = isA ? srcA[i] : srcB[i - TL::CHA];
+      const uint32_t off = kb0 + (c % 4) * 16;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (src >= 0) {
+        const uint8_t *g = (isA ? p.a_q : bq) + (int64_t)src * kbytes + off;
+        if (ALIGNED) {
+          v = *reinterpret_cast<const u32x4 *>(g);
+        } else {
+          uint8_t tmp[16];
+#pragma unroll
+          for (int b = 0; b < 16; ++b) tmp[b] = (off + b < kbytes) ? g[b] : 0;
+          __builtin_memcpy(&v, tmp, 16);
+        }
+      }
+      if (isA) ra[i] = v; else rb[i - TL::CHA] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const uint32_t c = tid + i * NT;
+      u32x2 v = {0u, 0u};
+      if (srcS[i] >= 0) {
+        const uint8_t *g = (c < (uint32_t)BM ? p.a_s : bs) + (int64_t)srcS[i] * kscales + ksc0;
+        if (ALIGNED) {
+          v = *reinterpret_cast<const u32x2 *>(g);
+        } else {
+          uint8_t tmp[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) tmp[b] = (ksc0 + b < kscales) ? g[b] : 0;
+          __builtin_memcpy(&v, tmp, 8);
+        }
+      }
+      rs[i] = v;
+    }
+  };
+  auto store_lds = [&](uint32_t buf) {
+    uint8_t *st = smem + buf * TL::STAGE;
+#pragma unroll
+    for (int i = 0; i < TL::CHA; ++i) {
+      const uint32_t c = tid + i * NT;
+      *reinterpret_cast<u32x4 *>(st + (c / 4) * ROWB + (c % 4) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < TL::CHB; ++i) {
+      const uint32_t c = tid + i * NT;
+      *reinterpret_cast<u32x4 *>(st + TL::OFF_B + (c / 4) * ROWB + (c % 4) * 16) = rb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SCH; ++i) {
+      const uint32_t c = tid + i * NT;
+      if (c < (uint32_t)(BM + BN)) *reinterpret_cast<u32x2 *>(st + TL::OFF_SA + c * SBY) = rs[i];
+    }
+  };
+
   const uint32_t wave = tid / 64, lane = tid % 64;
-  const uint32_t wm = wave / NW_N, wn = wave % NW_N;
+  const uint32_t wm = wave / NWN, wn = wave % NWN;
   const uint32_t l32 = lane % 32, lh = lane / 32;
 
   float16v acc[FM][FN];
@@ -191,160 +298,168 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmPa
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const uint32_t nsteps = (K + BK - 1) / BK;
-  for (uint32_t ks = 0; ks < nsteps; ++ks) {
-    const uint32_t kb0 = ks * KB;   // first packed byte of this step
-    const uint32_t ksc0 = ks * SB;  // first scale of this step
-    __syncthreads();  // previous step's LDS reads are done
-    // ---- packed codes: 8 x 16-byte chunks per row
-    for (uint32_t c = tid; c < (uint32_t)(BM + BN) * 8; c += NT) {
-      const bool isA = c < (uint32_t)BM * 8;
-      const uint32_t rho = (isA ? c : c - BM * 8) / 8, ch = c % 8;
-      const int32_t src = isA ? sRow[rho] : b_row(rho);
-      uint8_t *dst = (isA ? sA : sB) + rho * ROWB + ch * 16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (src >= 0) {
-        const uint8_t *g = (isA ? p.a_q : bq) + (int64_t)src * kbytes + kb0 + ch * 16;
-        if (ALIGNED) {
-          v = *reinterpret_cast<const u32x4 *>(g);
-        } else {
-          uint8_t tmp[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmp[i] = (kb0 + ch * 16 + i < kbytes) ? g[i] : 0;
-          __builtin_memcpy(&v, tmp, 16);
-        }
-      }
-      *reinterpret_cast<u32x4 *>(dst) = v;
-    }
-    // ---- block scales: 16 per row, converted to f16
-    for (uint32_t c = tid; c < (uint32_t)(BM + BN); c += NT) {
-      const bool isA = c < (uint32_t)BM;
-      const uint32_t rho = isA ? c : c - BM;
-      const int32_t src = isA ? sRow[rho] : b_row(rho);
-      uint8_t sc[16];
-      if (src >= 0) {
-        const uint8_t *g = (isA ? p.a_s : bs) + (int64_t)src * kscales + ksc0;
-        if (ALIGNED) {
-          u32x4 v = *reinterpret_cast<const u32x4 *>(g);
-          __builtin_memcpy(sc, &v, 16);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = (ksc0 + i < kscales) ? g[i] : 0;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] = 0;
-      }
-      _Float16 *dst = (isA ? sAs : sBs) + rho * SROWH;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i] = scale_f16(sc[i]);
-    }
-    __syncthreads();
-
-    // ---- fragments: lane (l32, lh) of fragment i reads row (wave row base + 32i + l32)
-    u32x4 pa[FM][4], pb[FN][4];
-    half8v sa[FM], sb[FN];
+  auto compute = [&](uint32_t buf) {
+    const uint8_t *st = smem + buf * TL::STAGE;
+    u32x4 pa[FM][2], pb[FN][2];
+    half2v sa[FM][2], sb[FN][2];  // (scale of block 2m, of block 2m+1) for m = 0, 1
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const uint32_t rho = wm * WM + i * 32 + l32;
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(sA + rho * ROWB + lh * 64);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pa[i][c] = src[c];
-      sa[i] = *reinterpret_cast<const half8v *>(sAs + rho * SROWH + lh * 8);
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(st + rho * ROWB + lh * 32);
+      pa[i][0] = src[0];
+      pa[i][1] = src[1];
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(st + TL::OFF_SA + rho * SBY + lh * 4);
+      sa[i][0] = scale_pair(w);       // blocks 0, 2 of the lane's four
+      sa[i][1] = scale_pair(w >> 8);  // blocks 1, 3
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const uint32_t rho = wn * WN + j * 32 + l32;
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(sB + rho * ROWB + lh * 64);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pb[j][c] = src[c];
-      sb[j] = *reinterpret_cast<const half8v *>(sBs + rho * SROWH + lh * 8);
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(st + TL::OFF_B + rho * ROWB + lh * 32);
+      pb[j][0] = src[0];
+      pb[j][1] = src[1];
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(st + TL::OFF_SB + rho * SBY + lh * 4);
+      sb[j][0] = scale_pair(w);
+      sb[j][1] = scale_pair(w >> 8);
     }
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < 8; ++t) {
+      // dword t covers block t/2 of the lane's four: scale_pair slot (t/2)%2, lane (t/2)/2
+      const int blk = t / 2;
       half8v av[FM], bv[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) av[i] = decode8(pa[i][t / 4][t % 4], sa[i][t / 2]);
+      for (int i = 0; i < FM; ++i) av[i] = decode8(pa[i][t / 4][t % 4], sa[i][blk % 2][blk / 2]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bv[j] = decode8(pb[j][t / 4][t % 4], sb[j][t / 2]);
+      for (int j = 0; j < FN; ++j) bv[j] = decode8(pb[j][t / 4][t % 4], sb[j][blk % 2][blk / 2]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  // ---------------------------------------------------------------- K loop
+  const uint32_t nsteps = (K + BK - 1) / BK;
+  load_global(0);
+  store_lds(0);
+  __syncthreads();
+  if (nsteps > 1) load_global(1);
+  for (uint32_t ks = 0; ks < nsteps; ++ks) {
+    compute(ks & 1);
+    if (ks + 1 < nsteps) store_lds((ks + 1) & 1);
+    __syncthreads();
+    if (ks + 2 < nsteps) load_global(ks + 2);
   }
 
-  // ---- epilogue.  Accumulator register r of lane (l32, lh) in a 32x32 tile
-  // holds row 8*(r/4) + 4*lh + (r%4), column l32.
+  // ---------------------------------------------------------------- epilogue
+  // Each wave stages one 32-row slab (its fragment row i) at a time in its own
+  // LDS region, then writes it out row by row.  Accumulator register r of lane
+  // (l32, lh) in a 32x32 tile holds row 8*(r/4) + 4*lh + (r%4), column l32.
+  constexpr int ROW_ELEMS = WN_OUT;
+  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;  // +16: bank spread
+  static_assert(TL::NW * 32 * ROW_BYTES <= 2 * TL::STAGE, "epilogue staging must fit");
   OutT *C = static_cast<OutT *>(p.c);
+  uint8_t *slab = smem + wave * 32 * ROW_BYTES;
+  const uint32_t col0 = tile_n * BN_OUT + wn * WN_OUT;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const uint32_t trow = wm * WM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-      const uint32_t row = row0 + trow;
-      if (row >= row_end) continue;
+      const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4);
+      OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
       if (SILU) {
-        const uint32_t col = tile_n * BN_OUT + wn * 32 + l32;
-        if (col < n_out) {
-          const float gt = acc[i][0][r] * out_scale;
-          const float up = acc[i][1][r] * out_scale;
-          store_out<OutT>(C + (int64_t)row * p.ldc + col, silu(gt) * up);
-        }
+#pragma unroll
+        for (int j = 0; j < HALF; ++j)
+          dst[j * 32 + l32] =
+              to_out<OutT>(silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale));
       } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const uint32_t col = tile_n * BN + wn * WN + j * 32 + l32;
-          if (col < n_out) store_out<OutT>(C + (int64_t)row * p.ldc + col, acc[i][j][r] * out_scale);
-        }
+        for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    // 32 rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
+    constexpr int VEC = 16 / (int)sizeof(OutT);
+    constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
+    const uint32_t rbase = row0 + wm * WM + i * 32;
+    for (int c = lane; c < 32 * CPR; c += 64) {
+      const uint32_t tr = c / CPR, cc = c % CPR;
+      const uint32_t row = rbase + tr;
+      const uint32_t col = col0 + cc * VEC;
+      if (row >= row_end) continue;
+      const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
+      OutT *g = C + (int64_t)row * p.ldc + col;
+      if (VSTORE && col + VEC <= n_out) {
+        *reinterpret_cast<u32x4 *>(g) = *reinterpret_cast<const u32x4 *>(srcp);
+      } else {
+        const OutT *sv = reinterpret_cast<const OutT *>(srcp);
+        for (int e = 0; e < VEC; ++e)
+          if (col + e < n_out) g[e] = sv[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <bool GROUPED, bool SILU, typename OutT>
-hipError_t launch_cfg(const GemmParams &p, uint32_t grid, bool aligned, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
-  constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  if (aligned)
-    gemm_kernel<BM, BN, WM, WN, GROUPED, true, SILU, OutT><<<grid, NT, 0, stream>>>(p);
-  else
-    gemm_kernel<BM, BN, WM, WN, GROUPED, false, SILU, OutT><<<grid, NT, 0, stream>>>(p);
+template <int BM, int BN, int WM, int WN, bool GROUPED, bool SILU, typename OutT>
+hipError_t launch_cfg(const GemmParams &p, uint32_t grid, bool aligned, bool vstore,
+                      hipStream_t stream) {
+  constexpr int NT = Tile<BM, BN, WM, WN>::NT;
+  if (aligned) {
+    if (vstore)
+      gemm_kernel<BM, BN, WM, WN, GROUPED, true, SILU, true, OutT><<<grid, NT, 0, stream>>>(p);
+    else
+      gemm_kernel<BM, BN, WM, WN, GROUPED, true, SILU, false, OutT><<<grid, NT, 0, stream>>>(p);
+  } else {
+    gemm_kernel<BM, BN, WM, WN, GROUPED, false, SILU, false, OutT><<<grid, NT, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
-bool is_aligned(const GemmParams &p) {
-  auto al = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
-  return p.K % BK == 0 && al(p.a_q) && al(p.a_s) && al(p.b_q) && al(p.b_s) &&
-         p.b_mstride_q % 16 == 0 && p.b_mstride_s % 16 == 0;
+bool operands_aligned(const GemmParams &p) {
+  auto al = [](const void *q, uintptr_t a) { return ((uintptr_t)q & (a - 1)) == 0; };
+  return p.K % BK == 0 && al(p.a_q, 16) && al(p.a_s, 8) && al(p.b_q, 16) && al(p.b_s, 8) &&
+         p.b_mstride_q % 16 == 0 && p.b_mstride_s % 8 == 0;
+}
+
+bool stores_aligned(const GemmParams &p, OutType out) {
+  const int64_t es = out == OutType::BF16 ? 2 : 4;
+  return ((uintptr_t)p.c & 15u) == 0 && (p.ldc * es) % 16 == 0;
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const uint32_t grid = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-  const bool al = is_aligned(p);
-  return out == OutType::BF16 ? launch_cfg<false, false, uint16_t>(p, grid, al, stream)
-                              : launch_cfg<false, false, float>(p, grid, al, stream);
+  constexpr int BM = 256, BN = 256;
+  const uint32_t grid = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  const bool al = operands_aligned(p), vs = stores_aligned(p, out);
+  return out == OutType::BF16
+             ? launch_cfg<BM, BN, 128, 128, false, false, uint16_t>(p, grid, al, vs, stream)
+             : launch_cfg<BM, BN, 128, 128, false, false, float>(p, grid, al, vs, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epilogue epi,
                                hipStream_t stream) {
   if (R == 0) return hipSuccess;
-  const uint32_t n_out = epi == Epilogue::SiluGate ? p.N / 2 : p.N;
-  const uint32_t bn_out = epi == Epilogue::SiluGate ? 64 : 128;
+  constexpr int BM = 128, BN = 256;
+  const bool silu = epi == Epilogue::SiluGate;
+  const uint32_t n_out = silu ? p.N / 2 : p.N;
+  const uint32_t bn_out = silu ? BN / 2 : BN;
   const uint32_t tiles_n = (n_out + bn_out - 1) / bn_out;
   // sum_e ceil(n_e / BM) <= R / BM + E
-  const uint64_t tiles_m = (uint64_t)(R + 127) / 128 + p.E;
+  const uint64_t tiles_m = (uint64_t)(R + BM - 1) / BM + p.E;
   const uint32_t grid = (uint32_t)(tiles_m * tiles_n);
-  const bool al = is_aligned(p);
-  if (epi == Epilogue::SiluGate)
-    return out == OutType::BF16 ? launch_cfg<true, true, uint16_t>(p, grid, al, stream)
-                                : launch_cfg<true, true, float>(p, grid, al, stream);
-  return out == OutType::BF16 ? launch_cfg<true, false, uint16_t>(p, grid, al, stream)
-                              : launch_cfg<true, false, float>(p, grid, al, stream);
+  const bool al = operands_aligned(p), vs = stores_aligned(p, out);
+  if (silu)
+    return out == OutType::BF16
+               ? launch_cfg<BM, BN, 64, 128, true, true, uint16_t>(p, grid, al, vs, stream)
+               : launch_cfg<BM, BN, 64, 128, true, true, float>(p, grid, al, vs, stream);
+  return out == OutType::BF16
+             ? launch_cfg<BM, BN, 64, 128, true, false, uint16_t>(p, grid, al, vs, stream)
+             : launch_cfg<BM, BN, 64, 128, true, false, float>(p, grid, al, vs, stream);
 }
 
 }  // namespace nvfp4
