@@ -80,8 +80,19 @@ const char *nvfp4_status_string(nvfp4_status status);
  *   r = 1 / (s*g);  code = E2M1(min(|x*r|, 6)) with the sign of x.
  * workspace  device scratch of at least nvfp4_quantize_workspace_size(rows,
  *         cols) bytes, 256-byte aligned (dynamic mode only; may be NULL when
- *         the size is 0 or static_global != 0).  Its contents on entry do not
- *         matter; it is clobbered.
+ *         static_global != 0).  It must be zero-filled before its first use
+ *         and then be left to this function: its first bytes hold the arrival
+ *         state of the single-read kernel, which every completed call leaves
+ *         ready for the next.  One workspace may serve any number of calls in
+ *         stream order; calls that overlap in time (different streams) need
+ *         separate workspaces.
+ * Dynamic mode reads x once from HBM when it fits in the register file of the
+ * GPU (about 42 M bf16 / 21 M fp32 elements on 256 CUs): one workgroup per CU
+ * keeps its share in registers while the workgroups exchange their maxima.
+ * If the workgroups are not all resident at once (other work occupying CUs),
+ * a workgroup whose bounded wait expires reads the whole tensor for the max
+ * itself: slower, same result.  Larger tensors take a two-pass path (amax,
+ * encode).
  * Precondition for the dynamic mode: amax == 0 or amax >= 2^-100.
  * Alignment: x 16-byte aligned and ld_x*elem_size a multiple of 16 for the
  * vectorised path; other layouts are accepted and take a slower path.
@@ -98,7 +109,8 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows,
  * g[b] = amax_b/2688.  This is the offline (static) weight quantization of the
  * per-expert matrices of an MoE (two-level scaling page, sub-section "The A4
  * side": weights are quantized offline; one global scale per tensor).
- * workspace: nvfp4_quantize_batched_workspace_size(batch, rows, cols) bytes. */
+ * workspace: nvfp4_quantize_batched_workspace_size(batch, rows, cols) bytes,
+ * 4-byte aligned; its contents on entry do not matter (it is clobbered). */
 size_t nvfp4_quantize_batched_workspace_size(int64_t batch, int64_t rows,
                                              int64_t cols);
 nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type,
@@ -119,7 +131,7 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type,
  * once in the epilogue; the result is rounded to c_type.
  * M, N >= 0; K > 0 and a multiple of 16.  c is [M][ldc] of c_type, ldc >= N.
  * a_g, b_g: device floats (read by the kernel; no host synchronization).
- * Faster paths need K % 256 == 0 and 16-byte aligned q rows; other shapes are
+ * Faster paths need K % 128 == 0 and 16-byte aligned q rows; other shapes are
  * handled by a general path with the same results.
  * ---------------------------------------------------------------------- */
 nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g,

@@ -43,10 +43,13 @@ size_t dtype_size(nvfp4_dtype t) { return t == NVFP4_F32 ? 4 : 2; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t quant_ws(int64_t batch, int64_t rows, int64_t cols) {
+// batched: per-matrix amax partials; single (batch 0 here means "single
+// tensor"): the resident-kernel state followed by the partials
+size_t quant_ws(int64_t batch, int64_t rows, int64_t cols, bool single) {
   if (batch <= 0 || rows < 0 || cols <= 0 || cols % 16 != 0) return 0;
   const uint64_t units = (uint64_t)rows * (uint64_t)(cols / 16);
-  return round_up((size_t)batch * quantize_partials_per_matrix(units) * sizeof(float), 256);
+  const size_t partials = round_up((size_t)batch * quantize_partials_per_matrix(units) * sizeof(float), 256);
+  return single ? kResidentStateBytes + partials : partials;
 }
 
 // shape rules shared by the quantize entry points
@@ -93,7 +96,7 @@ const char *nvfp4_status_string(nvfp4_status status) {
   return "NVFP4: unknown status";
 }
 
-size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) { return quant_ws(1, rows, cols); }
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) { return quant_ws(1, rows, cols, true); }
 
 nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows, int64_t cols,
                             int64_t ld_x, uint8_t *q, uint8_t *s, float *g, int static_global,
@@ -103,8 +106,8 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows, int
   if (rows > 0 && (!x || !q || !s)) return NVFP4_ERR_INVALID_ARG;
   if (rows > 0 && ld_x > kI32Max * 64ll) return NVFP4_ERR_INVALID_ARG;
   if (!static_global) {
-    const size_t need = quant_ws(1, rows, cols);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3u))
+    const size_t need = quant_ws(1, rows, cols, true);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
       return NVFP4_ERR_INVALID_ARG;
   } else if (rows == 0) {
     return NVFP4_OK;
@@ -112,12 +115,14 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows, int
   nvfp4_status st = check_device();
   if (st != NVFP4_OK) return st;
   const bool vec = aligned16(x) && (ld_x * (int64_t)dtype_size(x_type)) % 16 == 0;
-  QuantParams p = make_quant(x, rows, cols, ld_x, q, s, g, workspace, static_global ? 1 : 0);
-  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, stream));
+  ResidentState *rs = static_cast<ResidentState *>(workspace);
+  void *partials = workspace ? static_cast<uint8_t *>(workspace) + kResidentStateBytes : nullptr;
+  QuantParams p = make_quant(x, rows, cols, ld_x, q, s, g, partials, static_global ? 1 : 0);
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, rs, stream));
 }
 
 size_t nvfp4_quantize_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols) {
-  return quant_ws(batch, rows, cols);
+  return quant_ws(batch, rows, cols, false);
 }
 
 nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type, int64_t batch,
@@ -127,14 +132,14 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type, int64_t b
     return NVFP4_ERR_INVALID_ARG;
   if (batch == 0) return NVFP4_OK;
   if (!g || (rows > 0 && (!x || !q || !s))) return NVFP4_ERR_INVALID_ARG;
-  const size_t need = quant_ws(batch, rows, cols);
+  const size_t need = quant_ws(batch, rows, cols, false);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3u))
     return NVFP4_ERR_INVALID_ARG;
   nvfp4_status st = check_device();
   if (st != NVFP4_OK) return st;
   const bool vec = aligned16(x) && (cols * (int64_t)dtype_size(x_type)) % 16 == 0;
   QuantParams p = make_quant(x, rows, cols, cols, q, s, g, workspace, 0);
-  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, (uint32_t)batch, stream));
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, (uint32_t)batch, nullptr, stream));
 }
 
 nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g,

@@ -29,13 +29,13 @@ constexpr float kE4M3Max = 448.0f;
 //    steps (8 steps is 2^-6, which is code 0x08 as well);
 //  - from 2^-6 up, drop 20 of the float's 23 mantissa bits with round to
 //    nearest even, then rebias the exponent from 127 to 7.
+// Both are computed and one is selected, so the GPU runs it without branching.
 NVFP4_HD uint32_t e4m3_encode(float v) {
-  if (v < 0x1p-6f) return (uint32_t)__builtin_rintf(v * 512.0f);
+  const uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
   uint32_t b = f2u(v);
   b += 0x7FFFFu + ((b >> 20) & 1u);
-  uint32_t e = (b >> 23) - 120u;  // - 127 + 7
-  uint32_t m = (b >> 20) & 7u;
-  return (e << 3) | m;
+  const uint32_t nrm = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);  // exponent - 127 + 7
+  return v < 0x1p-6f ? sub : nrm;
 }
 
 // Value of a positive E4M3FN code (1..126) as float (exact).
@@ -62,13 +62,29 @@ NVFP4_HD uint32_t e2m1_encode(float y) {
   return c | ((f2u(y) >> 28) & 8u);
 }
 
-// Per-block scale step of the quantizer: returns the E4M3 code and writes the
-// encode multiplier r = 1 / (s * g).
+// fl(a / b), the IEEE quotient, from y = fl(1 / b) with two FMAs: q = fl(a y)
+// is within an ulp of a / b, r = a - q b is exact, and fl(q + r y) is the
+// correctly rounded quotient (Markstein's theorem, binary floating point with
+// a correctly rounded reciprocal; valid while the quotient is a normal float).
+NVFP4_HD float div_rn(float a, float b, float y) {
+  const float q = a * y;
+  const float r = __builtin_fmaf(-q, b, a);
+  return __builtin_fmaf(r, y, q);
+}
+
+// Block scale code from the block max (quantizer steps 3-4):
 //   s32 = bmax / (6 g) ; s = E4M3(min(s32, 448)) ; s = 2^-9 if it rounds to 0.
+// six_g = fl(6 g), inv_six_g = fl(1 / six_g).  Quotients below 2^-10 all give
+// code 1 and quotients above 448 all give 448, so the division only has to be
+// exact in between, where div_rn is.
+NVFP4_HD uint32_t block_scale_code(float bmax, float six_g, float inv_six_g) {
+  const uint32_t sc = e4m3_encode(__builtin_fminf(div_rn(bmax, six_g, inv_six_g), kE4M3Max));
+  return sc ? sc : 1u;
+}
+
+// Block scale code and its encode multiplier r = 1 / (s g).
 NVFP4_HD uint32_t block_scale(float bmax, float six_g, float g, float *r) {
-  float s32 = __builtin_fminf(bmax / six_g, kE4M3Max);
-  uint32_t sc = e4m3_encode(s32);
-  if (sc == 0u) sc = 1u;
+  const uint32_t sc = block_scale_code(bmax, six_g, 1.0f / six_g);
   *r = 1.0f / (e4m3_value(sc) * g);
   return sc;
 }

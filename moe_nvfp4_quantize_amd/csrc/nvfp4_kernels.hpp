@@ -12,6 +12,21 @@ namespace nvfp4 {
 // ---------------------------------------------------------------- quantize
 constexpr uint32_t kMaxPartials = 256;  // amax partials per matrix
 
+// Arrival state of the single-read (resident) quantize kernel; lives at the
+// start of the quantize workspace, which must be zero-filled before its first
+// use.  Every completed launch leaves it ready for the next one.
+constexpr uint32_t kMaxResidentWGs = 1024;
+struct ResidentState {
+  uint32_t parity;     // which slot array the current launch uses
+  uint32_t done;       // workgroups finished in the current launch
+  uint32_t fallbacks;  // workgroups whose wait expired (diagnostic; 0 when co-resident)
+  uint32_t pad;
+  // slot[p][w] = 0x80000000 | bits(max|x| of workgroup w): arrival flag and
+  // value in one word, written and read with relaxed atomics
+  uint32_t slot[2][kMaxResidentWGs];
+};
+constexpr size_t kResidentStateBytes = (sizeof(ResidentState) + 255) / 256 * 256;
+
 struct QuantParams {
   const void *x;      // first element of matrix 0
   int64_t ld;         // row stride of x, elements
@@ -28,7 +43,9 @@ struct QuantParams {
 };
 
 uint32_t quantize_partials_per_matrix(uint64_t units);
-hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, hipStream_t stream);
+// st: resident-kernel state (nullptr: two-pass path only)
+hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
+                           hipStream_t stream);
 
 // -------------------------------------------------------------------- GEMM
 struct GemmParams {

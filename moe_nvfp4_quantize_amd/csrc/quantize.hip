@@ -5,69 +5,140 @@
 // level 2: one FP32 scale per tensor) and sub-section "The A4 side: dynamic
 // activations" (activations quantized on the fly with the same rule).
 //
-// Two passes over the input:
-//   1. amax_partials: each workgroup reduces max|x| over a strided share of the
-//      16-element blocks and writes one partial per workgroup (no atomics, so no
-//      zero-initialised state is needed and the result is order independent);
-//   2. quantize: each workgroup first reduces the partials to amax and forms
-//      g = amax / 2688 (workgroup 0 stores it), then every thread encodes whole
-//      16-element blocks: block max, E4M3 block scale, one reciprocal, 16 E2M1
-//      codes packed into 8 bytes.
-// A thread owns a whole block, so the block max needs no cross-lane traffic;
-// consecutive threads own consecutive blocks of a row, so each wave reads
-// 2 KB (bf16) or 4 KB (fp32) of contiguous input and writes 512 B of codes and
-// 64 B of scales.
+// The dynamic global scale needs max|x| over the whole tensor before any block
+// can be encoded.  Two kernels implement that:
+//
+//  * resident (one HBM read): one workgroup per CU, 1024 threads (four waves
+//    per SIMD, up to 10 bf16 / 4 fp32 blocks per thread in 128 VGPRs) or 512
+//    threads (two waves per SIMD, up to 20 bf16 / 10 fp32 blocks in 256
+//    VGPRs).  Every thread loads its U 16-element blocks into registers and
+//    keeps their block maxima; each workgroup publishes its max and waits for
+//    all others', then every thread encodes its blocks from registers.  Used
+//    when the tensor fits in the register file (up to about 42 M bf16 or 21 M
+//    fp32 elements on 256 CUs).
+//  * two-pass (fallback for larger tensors, and the batched per-matrix form):
+//    an amax pass writes one partial per workgroup; the encode pass reduces the
+//    partials and re-reads x.
+//
+// Encoding one block (all float32, round to nearest even; the order of the
+// float32 steps is part of the specification and must not be fused):
+//    s = E4M3(min(bmax / (6 g), 448)), 2^-9 if that rounds to 0   [software;
+//                                      the quotient by div_rn, bit-identical
+//                                      to the IEEE division]
+//    r = 1 / (s g)                     [per-workgroup table over the 126 codes]
+//    y = x * r ;  code = E2M1(y)       [hardware v_cvt_scalef32_pk_fp4_f32 with
+//                                       unit scale: round to nearest even,
+//                                       saturating at 6, sign kept on zero]
+// A thread owns whole blocks, so the block max needs no cross-lane traffic;
+// consecutive threads own consecutive blocks, so a wave reads 2 KB (bf16) or
+// 4 KB (fp32) of contiguous input and writes 512 B of codes and 64 B of scales.
 #include "nvfp4_common.hpp"
 #include "nvfp4_format.hpp"
 #include "nvfp4_kernels.hpp"
+
+#include <algorithm>
 
 namespace nvfp4 {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;          // two-pass kernels
+constexpr uint32_t kSpinLimit = 1u << 15;  // arrival wait bound (tens of milliseconds)
 
-// 16 consecutive elements starting at p.  VEC: p is 16-byte aligned.
+// 16 consecutive elements starting at p, as raw words (bf16: 8 dwords holding
+// two values each; fp32: 16 dwords).  VEC: p is 16-byte aligned.
+template <typename T>
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  static constexpr int W = 8;
+};
+template <>
+struct Raw<float> {
+  static constexpr int W = 16;
+};
+
 template <typename T, bool VEC>
-__device__ __forceinline__ void load_block(const T *p, float v[16]);
-
-template <>
-__device__ __forceinline__ void load_block<uint16_t, true>(const uint16_t *p, float v[16]) {
-  const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
-  const uint4 a = p4[0];
-  const uint4 b = p4[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+__device__ __forceinline__ void load_raw(const T *p, uint32_t w[Raw<T>::W]) {
+  if (VEC) {
+    const uint4 *p4 = reinterpret_cast<const uint4 *>(p);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = bf16_lo(w[i]);
-    v[2 * i + 1] = bf16_hi(w[i]);
+    for (int i = 0; i < Raw<T>::W / 4; ++i) {
+      const uint4 t = p4[i];
+      w[4 * i] = t.x;
+      w[4 * i + 1] = t.y;
+      w[4 * i + 2] = t.z;
+      w[4 * i + 3] = t.w;
+    }
+  } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (uint32_t)p[2 * i] | ((uint32_t)p[2 * i + 1] << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = f2u(p[i]);
   }
 }
 
-template <>
-__device__ __forceinline__ void load_block<uint16_t, false>(const uint16_t *p, float v[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = u2f((uint32_t)p[i] << 16);
+template <typename T>
+__device__ __forceinline__ float elem(const uint32_t w[Raw<T>::W], int i) {
+  if constexpr (sizeof(T) == 2) return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+  else return u2f(w[i]);
 }
 
-template <>
-__device__ __forceinline__ void load_block<float, true>(const float *p, float v[16]) {
-  const float4 *p4 = reinterpret_cast<const float4 *>(p);
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// max |x| of a block.  bf16: on the packed bits (|x| is the low 15 bits of each
+// half, and non-negative floats order like their bit patterns), so the floats
+// need not be kept in registers until the encode.
+template <typename T>
+__device__ __forceinline__ float raw_max(const uint32_t w[Raw<T>::W]) {
+  if constexpr (sizeof(T) == 2) {
+    u16x2 m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 t = p4[i];
-    v[4 * i] = t.x;
-    v[4 * i + 1] = t.y;
-    v[4 * i + 2] = t.z;
-    v[4 * i + 3] = t.w;
+    for (int i = 0; i < 8; ++i)
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return u2f((uint32_t)(m2[0] > m2[1] ? m2[0] : m2[1]) << 16);
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(fabsf(elem<T>(w, i)), fabsf(elem<T>(w, i + 1))));
+    return m;
   }
 }
 
-template <>
-__device__ __forceinline__ void load_block<float, false>(const float *p, float v[16]) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = p[i];
+// Encode one block: scale code from the block max, 16 codes from x * r.  The
+// outputs are written once and not read back by this kernel: non-temporal
+// stores keep them from lingering dirty in L2.
+template <typename T>
+__device__ __forceinline__ void encode_block(const uint32_t w[Raw<T>::W], float bmax, float six_g,
+                                             float inv_six_g, const float *rtab, uint8_t *q,
+                                             uint8_t *s) {
+  const uint32_t sc = block_scale_code(bmax, six_g, inv_six_g);
+  const float r = rtab[sc];
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 0) * r, elem<T>(w, 1) * r, 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 2) * r, elem<T>(w, 3) * r, 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 4) * r, elem<T>(w, 5) * r, 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 6) * r, elem<T>(w, 7) * r, 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 8) * r, elem<T>(w, 9) * r, 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 10) * r, elem<T>(w, 11) * r, 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 12) * r, elem<T>(w, 13) * r, 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 14) * r, elem<T>(w, 15) * r, 1.0f, 3);
+  __builtin_nontemporal_store((uint64_t)lo | ((uint64_t)hi << 32), reinterpret_cast<uint64_t *>(q));
+  __builtin_nontemporal_store((uint8_t)sc, s);
 }
+
+// r = 1 / (s * g) for every positive E4M3 code s (index 1..126); one per thread.
+__device__ __forceinline__ void fill_rtab(float *rtab, float g) {
+  const uint32_t c = threadIdx.x;
+  if (c < 128) rtab[c] = (c >= 1u && c <= 126u) ? 1.0f / (e4m3_value(c) * g) : 0.0f;
+}
+
+__device__ __forceinline__ float global_from_amax(float amax) {
+  return amax > 0.0f ? amax / kGlobalDivisor : 1.0f;
+}
+
+// ------------------------------------------------------------ two-pass path
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) {
@@ -77,10 +148,9 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) 
   for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < p.units; u += gridDim.x * kThreads) {
     const uint32_t row = p.div_nbpr.div(u);
     const uint32_t blk = u - row * p.nbpr;
-    float v[16];
-    load_block<T, VEC>(x + (int64_t)row * p.ld + blk * 16, v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    uint32_t w[Raw<T>::W];
+    load_raw<T, VEC>(x + (int64_t)row * p.ld + blk * 16, w);
+    m = fmaxf(m, raw_max<T>(w));
   }
   m = block_max(m);
   if (threadIdx.x == 0) p.partials[(int64_t)b * p.P + blockIdx.x] = m;
@@ -88,6 +158,7 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) 
 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
+  __shared__ float rtab[128];
   const uint32_t b = blockIdx.y;
   float g;
   if (p.static_global) {
@@ -96,38 +167,135 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     float m = 0.0f;
     for (uint32_t i = threadIdx.x; i < p.P; i += kThreads) m = fmaxf(m, p.partials[(int64_t)b * p.P + i]);
     m = block_max(m);
-    g = m > 0.0f ? m / kGlobalDivisor : 1.0f;
+    g = global_from_amax(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) p.g[b] = g;
   }
-  const float six_g = 6.0f * g;
-
+  fill_rtab(rtab, g);
+  __syncthreads();
+  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g;
   const T *x = static_cast<const T *>(p.x) + (int64_t)b * p.x_mstride;
   uint8_t *q = p.q + (int64_t)b * p.q_mstride;
   uint8_t *s = p.s + (int64_t)b * p.s_mstride;
   for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < p.units; u += gridDim.x * kThreads) {
     const uint32_t row = p.div_nbpr.div(u);
     const uint32_t blk = u - row * p.nbpr;
-    float v[16];
-    load_block<T, VEC>(x + (int64_t)row * p.ld + blk * 16, v);
-    float bmax = 0.0f;
+    uint32_t w[Raw<T>::W];
+    load_raw<T, VEC>(x + (int64_t)row * p.ld + blk * 16, w);
+    // u == row * nbpr + blk and q/s rows are dense: offsets are u*8 and u
+    encode_block<T>(w, raw_max<T>(w), six_g, inv_six_g, rtab, q + (int64_t)u * 8, s + u);
+  }
+}
+
+// ------------------------------------------------------------ resident path
+
+// Max |x| over the whole tensor read by one workgroup alone: the way out when
+// the other workgroups of a launch do not all become resident in time.
+template <typename T, bool VEC>
+__device__ float whole_tensor_max(const QuantParams &p) {
+  const T *x = static_cast<const T *>(p.x);
+  float m = 0.0f;
+  for (uint32_t u = threadIdx.x; u < p.units; u += blockDim.x) {
+    const uint32_t row = p.div_nbpr.div(u);
+    uint32_t w[Raw<T>::W];
+    load_raw<T, VEC>(x + (int64_t)row * p.ld + (u - row * p.nbpr) * 16, w);
+    m = fmaxf(m, raw_max<T>(w));
+  }
+  return block_max(m);
+}
+
+// Single HBM read.  Cross-workgroup traffic is relaxed atomics on single words
+// only (no release/acquire fences, which on a multi-XCD GPU write back and
+// invalidate L2): workgroup w publishes 0x80000000 | bits(its max) into
+// slot[parity][w] and waits until slots 0..G-1 all carry the flag.  The other
+// parity's slots are cleared for the next launch, and the last workgroup to
+// finish flips the parity.  A wait that runs past its bound (workgroups not
+// co-resident) is not an error: that workgroup reads the whole tensor itself,
+// which yields the same max.
+template <typename T, bool VEC, int U, int NT>
+__global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentState *st) {
+  __shared__ float rtab[128];
+  __shared__ uint32_t s_fallback;
+  const uint32_t tid = threadIdx.x, G = gridDim.x;
+  const uint32_t stride = G * NT;
+  const T *x = static_cast<const T *>(p.x);
+  const uint32_t par = __hip_atomic_load(&st->parity, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u;
+  for (uint32_t i = blockIdx.x * NT + tid; i < kMaxResidentWGs; i += stride)
+    __hip_atomic_store(&st->slot[par ^ 1u][i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // phase 1: every block of this thread into registers, with its max
+  uint32_t w[U][Raw<T>::W];
+  float bmax[U];
+  float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
-    float r;
-    const uint32_t sc = block_scale(bmax, six_g, g, &r);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo |= e2m1_encode(v[i] * r) << (4 * i);
-      hi |= e2m1_encode(v[8 + i] * r) << (4 * i);
+  for (int i = 0; i < U; ++i) {
+    const uint32_t u = i * stride + blockIdx.x * NT + tid;
+    if (u < p.units) {
+      const uint32_t row = p.div_nbpr.div(u);
+      load_raw<T, VEC>(x + (int64_t)row * p.ld + (u - row * p.nbpr) * 16, w[i]);
     }
-    // u == row * nbpr + blk, and q/s rows are dense: offsets are u*8 and u
-    *reinterpret_cast<uint2 *>(q + (int64_t)u * 8) = make_uint2(lo, hi);
-    s[u] = (uint8_t)sc;
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const uint32_t u = i * stride + blockIdx.x * NT + tid;
+    bmax[i] = u < p.units ? raw_max<T>(w[i]) : 0.0f;
+    m = fmaxf(m, bmax[i]);
+  }
+  m = block_max(m);
+
+  // publish, then gather every workgroup's max
+  if (tid == 0) {
+    s_fallback = 0u;
+    __hip_atomic_store(&st->slot[par][blockIdx.x], 0x80000000u | f2u(m), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  float a = 0.0f;
+  for (uint32_t i = tid; i < G; i += NT) {
+    uint32_t v = 0;
+    for (uint32_t spin = 0;; ++spin) {
+      v = __hip_atomic_load(&st->slot[par][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v & 0x80000000u) break;
+      if (spin >= kSpinLimit) {
+        s_fallback = 1u;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    a = fmaxf(a, u2f(v & 0x7FFFFFFFu));
+  }
+  a = block_max(a);  // contains a barrier: s_fallback is settled
+  if (s_fallback) {
+    a = whole_tensor_max<T, VEC>(p);
+    if (tid == 0) __hip_atomic_fetch_add(&st->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const float g = global_from_amax(a);
+  if (blockIdx.x == 0 && tid == 0) p.g[0] = g;
+  fill_rtab(rtab, g);
+  __syncthreads();
+  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g;
+
+  // phase 2: encode from registers
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const uint32_t u = i * stride + blockIdx.x * NT + tid;
+    if (u < p.units) encode_block<T>(w[i], bmax[i], six_g, inv_six_g, rtab, p.q + (int64_t)u * 8, p.s + u);
+  }
+
+  // the last workgroup out hands the other slot array to the next launch
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&st->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == G - 1) {
+      __hip_atomic_store(&st->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&st->parity, par ^ 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
 template <typename T, bool VEC>
-hipError_t launch_typed(const QuantParams &p, uint32_t batch, uint32_t qgrid, hipStream_t stream) {
+hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t stream) {
+  uint64_t wg = ((uint64_t)p.units + kThreads - 1) / kThreads;
+  if (wg < 1) wg = 1;
+  const uint32_t qgrid = (uint32_t)(wg < 2048 ? wg : 2048);
   if (!p.static_global) {
     amax_partials_kernel<T, VEC><<<dim3(p.P, batch), kThreads, 0, stream>>>(p);
     hipError_t e = hipGetLastError();
@@ -135,6 +303,60 @@ hipError_t launch_typed(const QuantParams &p, uint32_t batch, uint32_t qgrid, hi
   }
   quantize_kernel<T, VEC><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+// Number of CUs of the current device (one resident workgroup fits per CU),
+// cached per device.
+uint32_t resident_capacity_wgs() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = cus > 0 ? cus : -1;
+  }
+  return cached[dev] > 0 ? (uint32_t)cached[dev] : 0u;
+}
+
+template <typename T, bool VEC, int U, int NT>
+hipError_t launch_resident_u(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
+  resident_kernel<T, VEC, U, NT><<<G, NT, 0, stream>>>(p, st);
+  return hipGetLastError();
+}
+
+// Blocks per thread U and workgroup size NT: 1024 threads (four waves per
+// SIMD, at most 128 VGPRs) while U stays small, 512 threads (256 VGPRs) for
+// the largest tensors.  Returns hipErrorInvalidValue when no variant fits.
+template <typename T, bool VEC>
+hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
+  const uint64_t n = p.units;
+  auto need = [&](uint64_t nt) { return (n + (uint64_t)G * nt - 1) / ((uint64_t)G * nt); };
+  const uint64_t u1024 = need(1024), u512 = need(512);
+  if constexpr (sizeof(T) == 2) {
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024>(p, st, G, stream);
+    if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024>(p, st, G, stream);
+    if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024>(p, st, G, stream);
+    if (u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024>(p, st, G, stream);
+    if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512>(p, st, G, stream);
+    if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512>(p, st, G, stream);
+  } else {
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024>(p, st, G, stream);
+    if (u512 <= 6) return launch_resident_u<T, VEC, 6, 512>(p, st, G, stream);
+    if (u512 <= 8) return launch_resident_u<T, VEC, 8, 512>(p, st, G, stream);
+    if (u512 <= 10) return launch_resident_u<T, VEC, 10, 512>(p, st, G, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// true when launch_resident has a variant for this many blocks on G workgroups
+bool resident_fits(uint64_t units, uint32_t G, bool bf16) {
+  const uint64_t cap = (uint64_t)G * 512 * (bf16 ? 20 : 10);
+  return units <= cap;
 }
 
 }  // namespace
@@ -145,16 +367,26 @@ uint32_t quantize_partials_per_matrix(uint64_t units) {
   return (uint32_t)(wg < kMaxPartials ? wg : kMaxPartials);
 }
 
-hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, hipStream_t stream) {
-  uint64_t wg = ((uint64_t)p.units + kThreads - 1) / kThreads;
-  if (wg < 1) wg = 1;
-  // enough workgroups to fill the chip several times; each reduces P partials
-  const uint32_t qgrid = (uint32_t)(wg < 2048 ? wg : 2048);
+hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
+                           hipStream_t stream) {
+  // single-read resident path: dynamic scale, one matrix, fits in registers
+  if (!p.static_global && batch == 1 && st != nullptr) {
+    const uint32_t cus = resident_capacity_wgs();
+    uint32_t G = (uint32_t)std::min<uint64_t>(((uint64_t)p.units + 511) / 512, cus);
+    G = std::min<uint32_t>(std::max<uint32_t>(G, 1u), kMaxResidentWGs);
+    if (cus > 0 && resident_fits(p.units, G, bf16)) {
+      if (bf16)
+        return vec ? launch_resident<uint16_t, true>(p, st, G, stream)
+                   : launch_resident<uint16_t, false>(p, st, G, stream);
+      return vec ? launch_resident<float, true>(p, st, G, stream)
+                 : launch_resident<float, false>(p, st, G, stream);
+    }
+  }
   if (bf16)
-    return vec ? launch_typed<uint16_t, true>(p, batch, qgrid, stream)
-               : launch_typed<uint16_t, false>(p, batch, qgrid, stream);
-  return vec ? launch_typed<float, true>(p, batch, qgrid, stream)
-             : launch_typed<float, false>(p, batch, qgrid, stream);
+    return vec ? launch_two_pass<uint16_t, true>(p, batch, stream)
+               : launch_two_pass<uint16_t, false>(p, batch, stream);
+  return vec ? launch_two_pass<float, true>(p, batch, stream)
+             : launch_two_pass<float, false>(p, batch, stream);
 }
 
 }  // namespace nvfp4

@@ -112,6 +112,20 @@ def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+# nvfp4_quantize's workspace must start zero-filled and then be reused: one per
+# (device, stream), grown (zero-filled again) when a larger one is needed.
+_QWS = {}
+
+
+def _quantize_ws(nbytes, device, stream):
+    key = (torch.device(device).index, int(stream.value or 0))
+    ws = _QWS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
+        _QWS[key] = ws
+    return ws
+
+
 # ------------------------------------------------------------------ quantize
 
 
@@ -136,11 +150,10 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
     static = g is not None
     if static:
         gg.copy_(g.reshape(1))
-    ws_bytes = lib.nvfp4_quantize_workspace_size(rows, cols)
-    ws = _ws(ws_bytes, x.device)
+    hs = _stream(stream)
+    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, hs)
     st = lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
-                            _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(),
-                            _stream(stream))
+                            _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_quantize", st)
     return q, s, gg
 

@@ -53,8 +53,9 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.nvfp4_quantize_workspace_size(0, 16) == 256
-    assert lib.nvfp4_quantize_workspace_size(8192, 5120) == 1024
+    base = lib.nvfp4_quantize_workspace_size(0, 16) - 256  # grid-barrier state
+    assert base >= 16 + 4 * 1024 and base % 256 == 0
+    assert lib.nvfp4_quantize_workspace_size(8192, 5120) == base + 1024
     assert lib.nvfp4_quantize_workspace_size(4, 15) == 0
     assert lib.nvfp4_quantize_batched_workspace_size(512, 2048, 4096) == 512 * 1024
     assert lib.nvfp4_moe_route_workspace_size(8192, 512, 10) >= 128 * 512 * 4
@@ -71,7 +72,7 @@ def _q(lib, **kw):
 @pytest.mark.parametrize("bad", [
     dict(cols=24), dict(cols=0), dict(rows=-1), dict(ld=16), dict(t=7), dict(x=None),
     dict(q=None), dict(s=None), dict(g=None), dict(ws=None), dict(wsb=8),
-    dict(ws=ctypes.c_void_p(0x1001)), dict(rows=2 ** 31, cols=16),
+    dict(ws=ctypes.c_void_p(0x1001)), dict(ws=ctypes.c_void_p(0x1080)), dict(rows=2 ** 31, cols=16),
 ])
 def test_quantize_rejects(lib, bad):
     assert _q(lib, **bad) == INVALID

@@ -160,3 +160,72 @@ def test_deterministic(B):
     b = B.nvfp4_quantize(x)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def _barrier_timeouts(B):
+    """Expired-wait counter of the single-read kernel in every cached workspace (0 when healthy)."""
+    torch.cuda.synchronize()
+    return sum(int(ws[8:12].view(torch.int32).item()) for ws in B._QWS.values())
+
+
+def test_midpoint_sweep_exact_scaling(B):
+    """Blocks whose scale makes r = 1, so y = x: codes follow E2M1 rounding directly.
+
+    Row 0 holds 2688 (g = 1); every other block holds a 6 (scale 1.0, r = 1)
+    and 15 values at, or a few float32 ulps around, grid points and midpoints.
+    """
+    vals = []
+    for m in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]:
+        for sgn in (1.0, -1.0):
+            v = np.float32(m * sgn)
+            vals.append(v)
+            up = dn = v
+            for _ in range(3):
+                up = np.nextafter(up, np.float32(np.inf), dtype=np.float32)
+                dn = np.nextafter(dn, np.float32(-np.inf), dtype=np.float32)
+                vals += [up, dn]
+    vals += [np.float32(0.0), np.float32(-0.0), np.float32(1e-30), np.float32(-1e-30),
+             np.float32(5.999999), np.float32(-5.9999995)]
+    vals = [v for v in vals if abs(v) <= 6.0]
+    nblk = -(-len(vals) // 15)
+    vals += [np.float32(0.0)] * (nblk * 15 - len(vals))
+    blocks = np.array(vals, dtype=np.float32).reshape(nblk, 15)
+    body = np.concatenate([np.full((nblk, 1), 6.0, np.float32), blocks], axis=1).reshape(1, -1)
+    head = np.zeros((1, body.shape[1]), np.float32)
+    head[0, 0] = 2688.0
+    x = np.concatenate([head, body])
+    for dt in (torch.float32, torch.bfloat16):
+        xt = torch.from_numpy(x).cuda().to(dt)
+        if dt == torch.bfloat16 and not np.array_equal(xt.float().cpu().numpy(), x):
+            xt = torch.from_numpy(x).cuda()  # values not bf16-exact: sweep in fp32 only
+        _check_full(B, xt)
+        rq, rs, rg = Q.quantize(x)
+        assert rg == 1.0 and np.all(rs[1] == 0x38)
+
+
+def test_two_pass_path_large_bf16(B):
+    """More blocks than the register file holds: the amax + encode passes."""
+    x = W.random_matrix(8192, 6144, seed=21, dtype=torch.bfloat16, device="cuda")
+    print("[quantize] two-pass 8192x6144 bf16", flush=True)
+    rows = torch.tensor([0, 1, 4097, 8191] + list(range(5, 8192, 509)), device="cuda")
+    _sampled(B, x, rows)
+
+
+def test_resident_fp32_at_capacity(B):
+    """fp32 h of the 128-expert MoE (32768 x 768) fills the resident path exactly."""
+    x = W.random_matrix(32768, 768, seed=22, device="cuda")
+    rows = torch.tensor([0, 32767] + list(range(3, 32768, 1021)), device="cuda")
+    _sampled(B, x, rows)
+
+
+def test_many_calls_reuse_the_workspace(B):
+    before = _barrier_timeouts(B)
+    for i, (r, c) in enumerate([(4096, 2048), (1, 16), (8192, 5120), (3, 48), (2000, 4096)] * 4):
+        x = W.random_matrix(r, c, seed=100 + i, dtype=torch.bfloat16, device="cuda") * (1.0 + i)
+        q, s, g = B.nvfp4_quantize(x)
+        assert g.item() == Q.global_scale(_host(x)), (i, r, c)
+        rr = torch.tensor([0, r - 1], device="cuda")
+        rq, rs, _ = Q.quantize(_host(x[rr]), g=g.item())
+        np.testing.assert_array_equal(s[rr].cpu().numpy(), rs)
+        np.testing.assert_array_equal(q[rr].cpu().numpy(), rq)
+    assert _barrier_timeouts(B) == before == 0
