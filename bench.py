@@ -53,6 +53,29 @@ def parse():
     return p.parse_args()
 
 
+def profiled_traffic(profile, source):
+    """HBM bytes per launch recorded in a committed rocprofv3 summary, or None.
+
+    The summary names the kernel source it was measured on (sha256); when that
+    file has changed since, the counters no longer describe it and None is
+    returned.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("#", " ", "|")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256") != digest or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def quant_bytes(numel, in_bytes):
     """Algorithmic HBM bytes of one quantize: read x, write codes (0.5 B) and scales (1/16 B)."""
     return numel * (in_bytes + 0.5 + 1.0 / 16.0)
@@ -125,15 +148,22 @@ def report_dense(st, timer, step_ms):
     else:
         roof = dict(bound="hbm", achieved=gemm_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=gemm_gbs / HBM_PEAK_GBS)
-    roof.update(kernel="nvfp4 gemm_kernel", traffic=None,
+    traffic = None
+    if st["name"] == "prefill_8192x5120":
+        traffic = profiled_traffic("gemm_prefill_8192x5120x25600.md", "moe_nvfp4_quantize_amd/csrc/gemm.hip")
+    roof.update(kernel="nvfp4 gemm_kernel", traffic=traffic,
                 per_launch=dict(flops=flops, algorithmic_bytes=gemm_bytes, avg_ms=gemm_ms))
     q_gbs = qbytes / (q_ms * 1e-3) / 1e9
     extra = dict(
         gemm=dict(avg_ms=gemm_ms, tflops=gemm_tflops, frac_f16_peak=gemm_tflops / F16_MFMA_PEAK_TFLOPS,
                   frac_fp4_peak=gemm_tflops / FP4_MFMA_PEAK_TFLOPS, gbs=gemm_gbs),
         quantize=dict(avg_ms=q_ms, gbs=q_gbs, frac_hbm=q_gbs / HBM_PEAK_GBS,
-                      algorithmic_bytes=qbytes, kernels="amax_partials + quantize"),
+                      algorithmic_bytes=qbytes, note="in-step interval, after the GEMM"),
     )
+    if "quantize_iso_ms" in st:
+        iso = st["quantize_iso_ms"]
+        extra["quantize_back_to_back"] = dict(avg_ms=iso, gbs=qbytes / (iso * 1e-3) / 1e9,
+                                              frac_hbm=qbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS)
     value = flops / (step_ms * 1e-3) / 1e12
     config = dict(workload=st["name"], M=M, N=N, K=K, x=cfg["x_dtype"], out=cfg["out"],
                   weights="NVFP4, quantized offline (static)", activations="NVFP4, dynamic, quantized in the step")
@@ -281,6 +311,18 @@ def main():
     for _ in range(args.steps):
         step(B, st, timer)
     torch.cuda.synchronize()
+
+    if kind == "linear":
+        # the activation quantizer alone, back to back (no GEMM in between)
+        for _ in range(3):
+            B.nvfp4_quantize(st["x"], out=st["xq"])
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record()
+        for _ in range(args.steps):
+            B.nvfp4_quantize(st["x"], out=st["xq"])
+        q1.record()
+        torch.cuda.synchronize()
+        st["quantize_iso_ms"] = q0.elapsed_time(q1) / args.steps
 
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
