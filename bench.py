@@ -151,7 +151,8 @@ def report_dense(st, timer, step_ms):
     traffic = None
     if st["name"] == "prefill_8192x5120":
         traffic = profiled_traffic("gemm_prefill_8192x5120x25600.md", "moe_nvfp4_quantize_amd/csrc/gemm.hip")
-    roof.update(kernel="nvfp4 gemm_kernel", traffic=traffic,
+    kernel = "nvfp4 gemm_dma_kernel" if K % 256 == 0 else "nvfp4 gemm_kernel"
+    roof.update(kernel=kernel, traffic=traffic,
                 per_launch=dict(flops=flops, algorithmic_bytes=gemm_bytes, avg_ms=gemm_ms))
     q_gbs = qbytes / (q_ms * 1e-3) / 1e9
     extra = dict(

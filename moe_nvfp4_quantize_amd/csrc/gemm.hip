@@ -20,8 +20,11 @@
 //    alike), and one packed multiply by 256 makes it s.
 //  * Packed operands stay packed until the last moment: global -> LDS moves
 //    0.5625 B per element (codes + scales), a quarter of an f16 GEMM's LDS
-//    traffic; LDS is double buffered and the next K step's global loads are in
-//    flight while the current one is multiplied.
+//    traffic.  Two kernels share the decode and the epilogue: gemm_dma_kernel
+//    (dense, K % 256 == 0, aligned operands; described where it is defined)
+//    and gemm_kernel (grouped, ragged K, unaligned operands), whose loads go
+//    through registers into a double-buffered LDS stage while the current one
+//    is multiplied.
 //  * Large wave tiles (up to 128 x 128 per wave) amortise each decoded
 //    fragment over 4 MFMAs in each direction: the decode work per MFMA falls as
 //    1/WM + 1/WN.
@@ -29,8 +32,8 @@
 //    operands (a GEMM sums over K, so any common order is exact): lane half h of
 //    a wave owns packed bytes [32h, 32h + 32) of each row (K elements
 //    [64h, 64h + 64), blocks 4h..4h+3), and MFMA step t consumes its dword t.
-//  * LDS rows of codes are padded to 80 bytes so the 16-byte reads of 8
-//    consecutive rows fall in distinct banks.
+//  * gemm_kernel pads LDS rows of codes to 80 bytes so the 16-byte reads of 8
+//    consecutive rows fall in distinct banks; gemm_dma_kernel swizzles them.
 //  * The epilogue stages each wave's 32-row slab through LDS so that global
 //    stores are 16 bytes per lane along a row.
 //  * Dense tiles are ordered XCD-aware: workgroup w runs on XCD w % 8, so each
@@ -403,6 +406,334 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
   }
 }
 
+
+// ====================================================================
+// Dense kernel for K % 256 == 0 and aligned operands: global -> LDS without
+// registers, software-pipelined decode.
+// ====================================================================
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Swizzle of the four 16-byte pieces of a 64-byte LDS row: piece c of row r
+// is stored at c ^ swz(r).  For the fragment reads (lane l reads piece c of row
+// r0 + l % 32) every aligned group of 8 rows then hits 8 different 16-byte
+// bank groups of a 128-byte window, and every aligned group of 16 rows 16
+// different ones of a 256-byte window.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+
+// 256 x 256 output tile, four waves of 128 x 128 (4 x 4 MFMA tiles each).
+//  * Codes and scales go from global memory straight into LDS
+//    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
+//    LDS), so no registers hold staged data and no LDS store instructions run.
+//  * Codes: three stages of one K step (128 elements: 64 bytes per row),
+//    fetched two steps ahead.  Scales: two chunks of eight K steps (64 bytes per
+//    row), so that a transfer reads 64 contiguous bytes of a row instead of 8;
+//    the next chunk is fetched during the first four steps of the current one.
+//  * Each step issues the same ten transfers (extra ones reload data that is
+//    not read any more, or rewrite identical bytes), so one wait count serves
+//    every step: at the mid-step barrier only the step's own transfers may be
+//    in flight.  The transfers are spread over the step's MFMAs so that the
+//    memory pipeline never backs up the wave's in-order issue.
+//  * Fragments are double buffered in registers by half step (16-byte piece):
+//    the second half of step k is read at the start of step k, the first half
+//    of step k + 1 right after the mid-step barrier.
+//  * Decode is software pipelined: while the 16 MFMAs of sub-step t run, the
+//    operands of sub-step t + 1 are decoded (one MFMA, then four VALU
+//    instructions, sixteen times).
+template <bool VSTORE, typename OutT>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
+  // code stages: [A 256 rows x 64 B][B 256 rows x 64 B], three of them
+  constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = 3;
+  // scale chunks: the scales of SC_STEPS K steps, [A 256 rows x 64 B][B ...], two of them
+  constexpr int SC_STEPS = 8, SC_B = BM * 64, SC_CHUNK = (BM + BN) * 64;
+  constexpr int OFF_SC = NSTAGE * CODE_STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[OFF_SC + 2 * SC_CHUNK];  // 160 KB
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const uint32_t K = p.K, kbytes = K / 2, kscales = K / 16;
+  const uint32_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  uint32_t tm, tn;
+  dense_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
+  const uint32_t row0 = tm * BM, col0n = tn * BN;
+  const uint32_t nsteps = K / 128;
+
+  // Global -> LDS transfers.  One transfer moves 64 lanes x 16 bytes into 1 KB
+  // of consecutive LDS; slot s = j * 256 + tid of a 16 KB operand region is
+  // row s / 4, physical 16-byte piece s % 4, which holds logical piece
+  // (s % 4) ^ swz(row).  Rows past the matrix read its last row (never stored).
+  // Byte offsets from the operand bases fit 32 bits (checked by the host).
+  uint32_t oa[4], ob[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t s = j * 256 + tid, r = s / 4, c = (s % 4) ^ swz(r);
+    const uint32_t ra = min(row0 + r, p.M - 1), rb = min(col0n + r, p.N - 1);
+    oa[j] = ra * kbytes + c * 16;
+    ob[j] = rb * kbytes + c * 16;
+  }
+  const uint32_t pc = (tid % 4) ^ swz(tid / 4);  // logical scale piece (same for every j)
+  // transfers 2 * part, 2 * part + 1 of step ks's codes (parts 0, 1: A; 2, 3: B)
+  auto issue_codes = [&](uint32_t ks, int part) {
+    uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
+    const uint8_t *qa = p.a_q + ks * 64, *qb = p.b_q + ks * 64;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * (part % 2) + jj;
+      if (part < 2)
+        __builtin_amdgcn_global_load_lds((glb_void *)(qa + oa[j]), (lds_void *)(st + j * 4096 + wave * 1024), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((glb_void *)(qb + ob[j]), (lds_void *)(st + CODE_B + j * 4096 + wave * 1024), 16, 0, 0);
+    }
+  };
+  // transfer j (possibly not known at compile time) of scale chunk c, for A
+  // and for B.  Transfer j covers rows 64 j + tid / 4: its offset is the j = 0
+  // offset plus a uniform step, clamped to the last row like the codes.  A
+  // piece past the end of the row reloads the chunk's first piece instead
+  // (K % 256 == 0 keeps that in the row).
+  const uint32_t sa0 = row0 * kscales + (tid / 4) * kscales + pc * 16;
+  const uint32_t sb0 = col0n * kscales + (tid / 4) * kscales + pc * 16;
+  const uint32_t sa_last = (p.M - 1) * kscales + pc * 16, sb_last = (p.N - 1) * kscales + pc * 16;
+  auto issue_scales = [&](uint32_t c, uint32_t j) {
+    uint8_t *st = smem + OFF_SC + (c % 2) * SC_CHUNK + j * 4096 + wave * 1024;
+    const uint32_t back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16;
+    const uint32_t step = j * 64 * kscales;
+    const uint32_t o_a = min(sa0 + step, sa_last), o_b = min(sb0 + step, sb_last);
+    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + o_a - back), (lds_void *)st, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void *)(p.b_s + c * 64 + o_b - back), (lds_void *)(st + SC_B), 16, 0, 0);
+  };
+
+  const uint32_t wm = wave / 2, wn = wave % 2;
+  const uint32_t l32 = lane % 32, lh = lane / 32;
+  // LDS byte offsets of this lane's fragment rows: codes (inside a stage) and
+  // scales (inside a chunk, without the step's piece)
+  uint32_t offA[FM][2], offB[FN][2], rowSA[FM], rowSB[FN], swA[FM], swB[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint32_t r = wm * WM + i * 32 + l32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) offA[i][h] = r * 64 + (((2 * lh + h) ^ swz(r)) * 16);
+    rowSA[i] = r * 64 + lh * 4;
+    swA[i] = swz(r);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const uint32_t r = wn * WN + j * 32 + l32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) offB[j][h] = CODE_B + r * 64 + (((2 * lh + h) ^ swz(r)) * 16);
+    rowSB[j] = SC_B + r * 64 + lh * 4;
+    swB[j] = swz(r);
+  }
+
+  float16v acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4 fa[FM], fb[FN];
+  uint32_t sa[FM], sb[FN];
+  auto read_half = [&](uint32_t ks, int h, u32x4 *xa, u32x4 *xb) {
+    const uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
+  };
+  // scale dword of step ks: piece (ks % 8) / 2 of the row's 64 bytes, half ks % 2
+  auto read_scales = [&](uint32_t ks, uint32_t *xa, uint32_t *xb) {
+    const uint8_t *st = smem + OFF_SC + ((ks / SC_STEPS) % 2) * SC_CHUNK + (ks % 2) * 8;
+    const uint32_t q = (ks % SC_STEPS) / 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const uint32_t *>(st + rowSB[j] + ((q ^ swB[j]) * 16));
+  };
+  // scale pairs of one step: block b of the lane's four is pair b % 2, element b / 2
+  auto pairs = [&](const uint32_t *ya, const uint32_t *yb, half2v (*pa)[2], half2v (*pb)[2]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      pa[i][0] = scale_pair(ya[i]);
+      pa[i][1] = scale_pair(ya[i] >> 8);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      pb[j][0] = scale_pair(yb[j]);
+      pb[j][1] = scale_pair(yb[j] >> 8);
+    }
+  };
+  // operands of MFMA step t (0..7) of a K step: dword t % 4 of the half-t/4
+  // fragments, block b = t / 2 of the lane's four
+  auto decode_step = [&](int t, const u32x4 *xa, const u32x4 *xb, half2v (*pa)[2],
+                         half2v (*pb)[2], half8v *oa8, half8v *ob8) {
+    const int b = t / 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) oa8[i] = decode8(xa[i][t % 4], pa[i][b % 2][b / 2]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) ob8[j] = decode8(xb[j][t % 4], pb[j][b % 2][b / 2]);
+  };
+  auto mfmas = [&](const half8v *oa8, const half8v *ob8) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa8[i], ob8[j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: one MFMA, then four VALU, sixteen times; NV memory transfers
+  // spread evenly (one after every 16 / NV MFMAs)
+  auto interleave = [&](auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;
+#pragma unroll
+    for (int k = 0; k < FM * FN; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      if (NV > 0 && k % (FM * FN / (NV > 0 ? NV : 1)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using NV0 = std::integral_constant<int, 0>;
+  using NV2 = std::integral_constant<int, 2>;
+  using NV4 = std::integral_constant<int, 4>;
+
+  // ---------------------------------------------------------------- K loop
+  // Software pipeline: while the MFMAs of step t run, the operands of step
+  // t + 1 are decoded; the next K step's first half is read from LDS while
+  // this step's second half is multiplied.  Codes are fetched two K steps
+  // ahead; scale chunk c + 1 is fetched during the first four steps of chunk c.
+  // Waits count transfers: at the mid-step barrier only this step's own
+  // transfers may still be in flight.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_scales(0, j);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue_codes(0, q);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue_codes(min(1u, nsteps - 1), q);
+  wait_vm<8>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_half(0, 0, fa, fb);
+  read_scales(0, sa, sb);
+  wait_lgkm0();
+  half2v spa[FM][2], spb[FN][2];
+  pairs(sa, sb, spa, spb);
+  half8v av[2][FM], bv[2][FN];
+  decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
+  for (uint32_t ks = 0; ks < nsteps; ++ks) {
+    // Every step issues ten transfers, so that one wait count fits all steps:
+    // the codes of step ks + 2 (near the end: of the last step again, into a
+    // stage nobody reads any more) and two transfers of a scale chunk (the next
+    // chunk during a chunk's first four steps, else the current chunk again:
+    // rewriting bytes with identical values is harmless to concurrent readers).
+    const uint32_t code_step = min(ks + 2, nsteps - 1);
+    const uint32_t part = ks % SC_STEPS, chunk = ks / SC_STEPS;
+    const uint32_t sc_chunk = (part < 4 && (chunk + 1) * SC_STEPS < nsteps) ? chunk + 1 : chunk;
+    u32x4 ha[FM], hb[FN];
+    read_half(ks, 1, ha, hb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mfmas(av[t & 1], bv[t & 1]);
+      if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+      else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
+      issue_codes(code_step, t);
+      if (t == 3) issue_scales(sc_chunk, part % 4);
+      if (t < 3) interleave(NV2());
+      else interleave(NV4());
+    }
+    wait_vm<10>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // the next step's first half (at the last step: stale data, never used)
+    uint32_t na[FM], nb[FN];
+    read_half(ks + 1, 0, fa, fb);
+    read_scales(ks + 1, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    half2v npa[FM][2], npb[FN][2];
+#pragma unroll
+    for (int t = 4; t < 8; ++t) {
+      mfmas(av[t & 1], bv[t & 1]);
+      if (t < 7) {
+        decode_step(t + 1, ha, hb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+      } else {
+        // keep the next step's operands from being used (and waited for) earlier
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
+        pairs(na, nb, npa, npb);
+        decode_step(0, fa, fb, npa, npb, av[0], bv[0]);
+      }
+      interleave(NV0());
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      spa[i][0] = npa[i][0];
+      spa[i][1] = npa[i][1];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      spb[j][0] = npb[j][0];
+      spb[j][1] = npb[j][1];
+    }
+  }
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // ---------------------------------------------------------------- epilogue
+  const float out_scale = (*p.a_g) * (*p.b_g);
+  constexpr int ROW_ELEMS = WN;
+  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;
+  static_assert(4 * 32 * ROW_BYTES <= OFF_SC, "epilogue staging must fit");
+  OutT *C = static_cast<OutT *>(p.c);
+  uint8_t *slab = smem + wave * 32 * ROW_BYTES;
+  const uint32_t col0 = col0n + wn * WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4);
+      OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    constexpr int VEC = 16 / (int)sizeof(OutT);
+    constexpr int CPR = ROW_ELEMS / VEC;
+    const uint32_t rbase = row0 + wm * WM + i * 32;
+    for (int c = lane; c < 32 * CPR; c += 64) {
+      const uint32_t tr = c / CPR, cc = c % CPR;
+      const uint32_t row = rbase + tr;
+      const uint32_t col = col0 + cc * VEC;
+      if (row >= p.M) continue;
+      const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
+      OutT *g = C + (int64_t)row * p.ldc + col;
+      if (VSTORE && col + VEC <= p.N) {
+        *reinterpret_cast<u32x4 *>(g) = *reinterpret_cast<const u32x4 *>(srcp);
+      } else {
+        const OutT *sv = reinterpret_cast<const OutT *>(srcp);
+        for (int e = 0; e < VEC; ++e)
+          if (col + e < p.N) g[e] = sv[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int BM, int BN, int WM, int WN, bool GROUPED, bool SILU, typename OutT>
 hipError_t launch_cfg(const GemmParams &p, uint32_t grid, bool aligned, bool vstore,
                       hipStream_t stream) {
@@ -436,6 +767,18 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
   constexpr int BM = 256, BN = 256;
   const uint32_t grid = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const bool al = operands_aligned(p), vs = stores_aligned(p, out);
+  const uint64_t kb = p.K / 2;
+  const bool fits32 = (uint64_t)p.M * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32);
+  if (al && fits32 && p.K % 256 == 0) {
+    if (out == OutType::BF16) {
+      if (vs) gemm_dma_kernel<true, uint16_t><<<grid, 256, 0, stream>>>(p);
+      else gemm_dma_kernel<false, uint16_t><<<grid, 256, 0, stream>>>(p);
+    } else {
+      if (vs) gemm_dma_kernel<true, float><<<grid, 256, 0, stream>>>(p);
+      else gemm_dma_kernel<false, float><<<grid, 256, 0, stream>>>(p);
+    }
+    return hipGetLastError();
+  }
   return out == OutType::BF16
              ? launch_cfg<BM, BN, 128, 128, false, false, uint16_t>(p, grid, al, vs, stream)
              : launch_cfg<BM, BN, 128, 128, false, false, float>(p, grid, al, vs, stream);
