@@ -216,7 +216,7 @@ def report_moe(st, timer, step_ms):
     gu_ms = timer.mean_ms("gate_up")
     gu_tflops = f_gu / (gu_ms * 1e-3) / 1e12
     roof = dict(bound="mfma", achieved=gu_tflops, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel="nvfp4 gemm_kernel (grouped, SiLU gate)",
+                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel="nvfp4 gemm_dma_kernel (grouped, SiLU gate)" if H % 256 == 0 else "nvfp4 gemm_kernel (grouped, SiLU gate)",
                 traffic=None, per_launch=dict(flops=f_gu, avg_ms=gu_ms))
     parts = {n: timer.mean_ms(n) for n in timer.names}
     d_ms = parts["down"]

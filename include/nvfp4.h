@@ -170,7 +170,8 @@ nvfp4_status nvfp4_moe_route(const float *logits, int64_t T, int32_t E,
  * For every expert e and routed row r in [offsets[e], offsets[e+1]):
  *   acc[r][n] = a_g * w_g[e] * sum_k A_hat[src(r)][k] * W_hat[e][n][k]
  * where src(r) = src_row[r] if src_row != NULL (row gather fused into the
- * operand load) else r.
+ * operand load) else r.  Every src(r) must lie in [0, a_rows): device-side
+ * contents (src_row, expert_offsets) are trusted, not checked.
  * a_q/a_s/a_g  NVFP4 source activations [a_rows][K] (one global scale).
  * expert_offsets  int32 [E+1] on the device, non-decreasing, offsets[0] = 0,
  *              offsets[E] <= R (rows past offsets[E] are not written).

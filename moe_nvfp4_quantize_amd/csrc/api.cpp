@@ -207,6 +207,7 @@ nvfp4_status nvfp4_moe_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, cons
   p.M = (uint32_t)R; p.N = (uint32_t)N; p.K = (uint32_t)K;
   p.c = c;
   p.ldc = epilogue == NVFP4_EPI_SILU_GATE ? N / 2 : N;
+  p.a_rows = (uint32_t)a_rows;
   p.src_row = src_row;
   p.expert_offsets = expert_offsets;
   p.E = (uint32_t)E;

@@ -425,11 +425,13 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Swizzle of the four 16-byte pieces of a 64-byte LDS row: piece c of row r
-// is stored at c ^ swz(r).  For the fragment reads (lane l reads piece c of row
-// r0 + l % 32) every aligned group of 8 rows then hits 8 different 16-byte
-// bank groups of a 128-byte window, and every aligned group of 16 rows 16
-// different ones of a 256-byte window.
-__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+// is stored at c ^ swz(r).  A 16-byte read of 64 lanes is served 16 lanes
+// (256 bytes, all 64 banks) at a time; in the fragment reads lane l reads
+// piece c of row r0 + l % 32, so 16 consecutive rows must cover the 16
+// distinct 16-byte slots of a 256-byte window: rows r % 4 give the 64-byte
+// quarter, swz(r) = (r / 4) % 4 the piece inside it (measured on gfx950:
+// no bank conflicts, where an unswizzled layout shows 3 of 4 LDS cycles lost).
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
 
 // 256 x 256 output tile, four waves of 128 x 128 (4 x 4 MFMA tiles each).
 //  * Codes and scales go from global memory straight into LDS
@@ -450,67 +452,148 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) ^ (r >> 3
 //  * Decode is software pipelined: while the 16 MFMAs of sub-step t run, the
 //    operands of sub-step t + 1 are decoded (one MFMA, then four VALU
 //    instructions, sixteen times).
-template <bool VSTORE, typename OutT>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4;
-  // code stages: [A 256 rows x 64 B][B 256 rows x 64 B], three of them
+  constexpr int BN = 256, WM = BM / 2, WN = 128, FM = WM / 32, FN = 4, HALF = FN / 2;
+  static_assert(BM == 128 || BM == 192 || BM == 256, "tile height");
+  static_assert(!SILU || GROUPED, "the SiLU epilogue is a grouped-GEMM epilogue");
+  // transfers (64 lanes x 16 bytes) per operand: per code stage, and per scale chunk
+  constexpr int TA = BM / 64, TB = BN / 64, TN = TA + TB;
+  // code stages: [A BM rows x 64 B][B 256 rows x 64 B], three of them
   constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = 3;
-  // scale chunks: the scales of SC_STEPS K steps, [A 256 rows x 64 B][B ...], two of them
+  // scale chunks: the scales of SC_STEPS K steps, [A BM rows x 64 B][B ...], two of them
   constexpr int SC_STEPS = 8, SC_B = BM * 64, SC_CHUNK = (BM + BN) * 64;
   constexpr int OFF_SC = NSTAGE * CODE_STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[OFF_SC + 2 * SC_CHUNK];  // 160 KB
+  constexpr uint32_t BN_OUT = SILU ? BN / 2 : BN;
+  constexpr int WN_OUT = SILU ? WN / 2 : WN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[OFF_SC + 2 * SC_CHUNK];
+  // set-up tables, in LDS that the transfers overwrite only after the set-up:
+  // the grouped tile search's prefix sums, its result, the tile's source rows
+  uint32_t *scan = reinterpret_cast<uint32_t *>(smem);
+  int32_t *sInfo = reinterpret_cast<int32_t *>(smem + 1024);
+  int32_t *sRow = reinterpret_cast<int32_t *>(smem + 2048);  // -1 past the end
 
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const uint32_t K = p.K, kbytes = K / 2, kscales = K / 16;
-  const uint32_t tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
-  uint32_t tm, tn;
-  dense_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
-  const uint32_t row0 = tm * BM, col0n = tn * BN;
+  const uint32_t n_out = SILU ? p.N / 2 : p.N;
+  const uint32_t tiles_n = (n_out + BN_OUT - 1) / BN_OUT;
   const uint32_t nsteps = K / 128;
 
-  // Global -> LDS transfers.  One transfer moves 64 lanes x 16 bytes into 1 KB
-  // of consecutive LDS; slot s = j * 256 + tid of a 16 KB operand region is
-  // row s / 4, physical 16-byte piece s % 4, which holds logical piece
-  // (s % 4) ^ swz(row).  Rows past the matrix read its last row (never stored).
-  // Byte offsets from the operand bases fit 32 bits (checked by the host).
-  uint32_t oa[4], ob[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t s = j * 256 + tid, r = s / 4, c = (s % 4) ^ swz(r);
-    const uint32_t ra = min(row0 + r, p.M - 1), rb = min(col0n + r, p.N - 1);
-    oa[j] = ra * kbytes + c * 16;
-    ob[j] = rb * kbytes + c * 16;
-  }
-  const uint32_t pc = (tid % 4) ^ swz(tid / 4);  // logical scale piece (same for every j)
-  // transfers 2 * part, 2 * part + 1 of step ks's codes (parts 0, 1: A; 2, 3: B)
-  auto issue_codes = [&](uint32_t ks, int part) {
-    uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
-    const uint8_t *qa = p.a_q + ks * 64, *qb = p.b_q + ks * 64;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * (part % 2) + jj;
-      if (part < 2)
-        __builtin_amdgcn_global_load_lds((glb_void *)(qa + oa[j]), (lds_void *)(st + j * 4096 + wave * 1024), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds((glb_void *)(qb + ob[j]), (lds_void *)(st + CODE_B + j * 4096 + wave * 1024), 16, 0, 0);
+  // ---------------------------------------------------------------- tile
+  uint32_t tile_n, row0, row_end;
+  const uint8_t *bq = p.b_q, *bs = p.b_s;
+  float b_g;
+  if (!GROUPED) {
+    const uint32_t tiles_m = (p.M + BM - 1) / BM;
+    uint32_t tm;
+    dense_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tile_n);
+    row0 = tm * BM;
+    row_end = p.M;
+    b_g = *p.b_g;
+  } else {
+    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM)
+    tile_n = blockIdx.x % tiles_n;
+    const uint32_t tile_mm = blockIdx.x / tiles_n;
+    if (tid == 0) sInfo[0] = -1;
+    uint32_t base = 0;
+    for (uint32_t c0 = 0; c0 < p.E; c0 += 256) {
+      const uint32_t e = c0 + tid;
+      uint32_t cnt = 0, lo = 0;
+      if (e < p.E) {
+        lo = (uint32_t)p.expert_offsets[e];
+        cnt = ((uint32_t)p.expert_offsets[e + 1] - lo + BM - 1) / BM;
+      }
+      scan[tid] = cnt;
+      __syncthreads();
+      for (uint32_t off = 1; off < 256; off <<= 1) {
+        const uint32_t v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+      }
+      const uint32_t incl = base + scan[tid];
+      const uint32_t excl = incl - cnt;
+      if (e < p.E && cnt && tile_mm >= excl && tile_mm < incl) {
+        sInfo[0] = (int32_t)e;
+        sInfo[1] = (int32_t)(lo + (tile_mm - excl) * BM);
+      }
+      base += scan[255];
+      __syncthreads();
     }
+    if (sInfo[0] < 0) return;  // past the last tile: the whole workgroup leaves
+    const uint32_t e = (uint32_t)sInfo[0];
+    row0 = (uint32_t)sInfo[1];
+    row_end = (uint32_t)p.expert_offsets[e + 1];
+    bq += (int64_t)e * p.b_mstride_q;
+    bs += (int64_t)e * p.b_mstride_s;
+    b_g = p.b_g[e];
+  }
+  const float out_scale = (*p.a_g) * b_g;
+  for (uint32_t r = tid; r < BM; r += 256) {
+    const uint32_t row = row0 + r;
+    int32_t src = -1;
+    if (row < row_end) src = (GROUPED && p.src_row) ? p.src_row[row] : (int32_t)row;
+    sRow[r] = src;
+  }
+  // B-tile row rho -> weight row (or -1 past N).  With SILU, in every wave the
+  // first FN/2 fragments hold gate columns and the last FN/2 the matching up
+  // columns (weight rows n and N/2 + n).
+  auto b_row = [&](uint32_t rho) -> int32_t {
+    if (SILU) {
+      const uint32_t half = p.N / 2;
+      const uint32_t wn = rho / WN, j = (rho % WN) / 32, c = rho % 32;
+      const uint32_t col = tile_n * BN_OUT + wn * (WN / 2) + (j % HALF) * 32 + c;
+      if (col >= half) return -1;
+      return (int32_t)(j < (uint32_t)HALF ? col : half + col);
+    }
+    const uint32_t n = tile_n * BN + rho;
+    return n < p.N ? (int32_t)n : -1;
   };
-  // transfer j (possibly not known at compile time) of scale chunk c, for A
-  // and for B.  Transfer j covers rows 64 j + tid / 4: its offset is the j = 0
-  // offset plus a uniform step, clamped to the last row like the codes.  A
+  __syncthreads();
+
+  // Global -> LDS transfers.  One transfer moves 64 lanes x 16 bytes into 1 KB
+  // of consecutive LDS: transfer j of an operand covers slots s = j * 256 + tid,
+  // i.e. tile row s / 4, physical 16-byte piece s % 4, which holds logical
+  // piece (s % 4) ^ swz(row) = pc for every j.  Rows past the end read a valid
+  // row instead (results never stored).  Byte offsets from the operand bases
+  // fit 32 bits (checked by the host).
+  const uint32_t pc = (tid % 4) ^ swz(tid / 4);
+  u32x4 oa = {0, 0, 0, 0}, ob, osa = {0, 0, 0, 0}, osb;
+  const int32_t a_fallback = sRow[0];  // the tile's first row always exists
+#pragma unroll
+  for (int j = 0; j < TA; ++j) {
+    const int32_t src = sRow[j * 64 + tid / 4];
+    const uint32_t ra = GROUPED ? (uint32_t)(src >= 0 ? src : a_fallback)
+                                : min(row0 + j * 64 + tid / 4, p.M - 1);
+    oa[j] = ra * kbytes + pc * 16;
+    osa[j] = ra * kscales + pc * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int32_t w = b_row(j * 64 + tid / 4);
+    const uint32_t rb = (uint32_t)(w >= 0 ? w : 0);
+    ob[j] = rb * kbytes + pc * 16;
+    osb[j] = rb * kscales + pc * 16;
+  }
+  __syncthreads();  // every wave is done with the set-up tables
+  // code transfer q (0 .. TN - 1; A first) of step ks
+  auto issue_code = [&](uint32_t ks, int q) {
+    uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
+    if (q < TA)
+      __builtin_amdgcn_global_load_lds((glb_void *)(p.a_q + ks * 64 + oa[q]), (lds_void *)(st + q * 4096 + wave * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + ob[q - TA]), (lds_void *)(st + CODE_B + (q - TA) * 4096 + wave * 1024), 16, 0, 0);
+  };
+  // scale transfers of chunk c: A transfer ja and B transfer jb (both possibly
+  // not known at compile time: vector selects, no indexing into memory).  A
   // piece past the end of the row reloads the chunk's first piece instead
   // (K % 256 == 0 keeps that in the row).
-  const uint32_t sa0 = row0 * kscales + (tid / 4) * kscales + pc * 16;
-  const uint32_t sb0 = col0n * kscales + (tid / 4) * kscales + pc * 16;
-  const uint32_t sa_last = (p.M - 1) * kscales + pc * 16, sb_last = (p.N - 1) * kscales + pc * 16;
-  auto issue_scales = [&](uint32_t c, uint32_t j) {
-    uint8_t *st = smem + OFF_SC + (c % 2) * SC_CHUNK + j * 4096 + wave * 1024;
+  auto issue_scales = [&](uint32_t c, uint32_t ja, uint32_t jb) {
+    uint8_t *st = smem + OFF_SC + (c % 2) * SC_CHUNK + wave * 1024;
     const uint32_t back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16;
-    const uint32_t step = j * 64 * kscales;
-    const uint32_t o_a = min(sa0 + step, sa_last), o_b = min(sb0 + step, sb_last);
-    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + o_a - back), (lds_void *)st, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void *)(p.b_s + c * 64 + o_b - back), (lds_void *)(st + SC_B), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + osa[ja] - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + osb[jb] - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
   };
 
   const uint32_t wm = wave / 2, wn = wave % 2;
@@ -574,8 +657,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       pb[j][1] = scale_pair(yb[j] >> 8);
     }
   };
-  // operands of MFMA step t (0..7) of a K step: dword t % 4 of the half-t/4
-  // fragments, block b = t / 2 of the lane's four
+  // operands of MFMA sub-step t (0..7) of a K step: dword t % 4 of the
+  // half-t/4 fragments, block b = t / 2 of the lane's four
   auto decode_step = [&](int t, const u32x4 *xa, const u32x4 *xb, half2v (*pa)[2],
                          half2v (*pb)[2], half8v *oa8, half8v *ob8) {
     const int b = t / 2;
@@ -591,36 +674,39 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa8[i], ob8[j], acc[i][j], 0, 0, 0);
   };
-  // interleave: one MFMA, then four VALU, sixteen times; NV memory transfers
-  // spread evenly (one after every 16 / NV MFMAs)
+  // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), FM * FN
+  // times; NV memory transfers spread evenly
   auto interleave = [&](auto nv_tag) {
-    constexpr int NV = decltype(nv_tag)::value;
+    constexpr int NV = decltype(nv_tag)::value, NM = FM * FN;
+    constexpr int VPM = (8 * (FM + FN) + NM - 1) / NM;
 #pragma unroll
-    for (int k = 0; k < FM * FN; ++k) {
+    for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      if (NV > 0 && k % (FM * FN / (NV > 0 ? NV : 1)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      if (NV > 0 && k % (NM / (NV > 0 ? NV : 1)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  using NV0 = std::integral_constant<int, 0>;
-  using NV2 = std::integral_constant<int, 2>;
-  using NV4 = std::integral_constant<int, 4>;
+  // code transfers placed in MFMA sub-step t (0..3) of the first half
+  auto codes_in = [](int t) { return ((t + 1) * TN + 3) / 4 - (t * TN + 3) / 4; };
 
   // ---------------------------------------------------------------- K loop
-  // Software pipeline: while the MFMAs of step t run, the operands of step
-  // t + 1 are decoded; the next K step's first half is read from LDS while
-  // this step's second half is multiplied.  Codes are fetched two K steps
-  // ahead; scale chunk c + 1 is fetched during the first four steps of chunk c.
-  // Waits count transfers: at the mid-step barrier only this step's own
-  // transfers may still be in flight.
+  // Software pipeline: while the MFMAs of sub-step t run, the operands of
+  // sub-step t + 1 are decoded; the next K step's first half is read from LDS
+  // while this step's second half is multiplied.  Codes are fetched two K
+  // steps ahead; scale chunk c + 1 during the first four steps of chunk c.
+  // Every step issues TN + 2 transfers (near the end the last step's codes
+  // again, into a stage nobody reads any more; outside the first four steps of
+  // a chunk the current chunk's scales again, rewriting identical bytes), so
+  // at the mid-step barrier one wait count leaves exactly this step's own
+  // transfers in flight.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) issue_scales(0, j);
+  for (int j = 0; j < 4; ++j) issue_scales(0, j % TA, j);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) issue_codes(0, q);
+  for (int q = 0; q < TN; ++q) issue_code(0, q);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) issue_codes(min(1u, nsteps - 1), q);
-  wait_vm<8>();
+  for (int q = 0; q < TN; ++q) issue_code(min(1u, nsteps - 1), q);
+  wait_vm<TN>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   read_half(0, 0, fa, fb);
@@ -631,11 +717,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   half8v av[2][FM], bv[2][FN];
   decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
   for (uint32_t ks = 0; ks < nsteps; ++ks) {
-    // Every step issues ten transfers, so that one wait count fits all steps:
-    // the codes of step ks + 2 (near the end: of the last step again, into a
-    // stage nobody reads any more) and two transfers of a scale chunk (the next
-    // chunk during a chunk's first four steps, else the current chunk again:
-    // rewriting bytes with identical values is harmless to concurrent readers).
     const uint32_t code_step = min(ks + 2, nsteps - 1);
     const uint32_t part = ks % SC_STEPS, chunk = ks / SC_STEPS;
     const uint32_t sc_chunk = (part < 4 && (chunk + 1) * SC_STEPS < nsteps) ? chunk + 1 : chunk;
@@ -647,12 +728,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       mfmas(av[t & 1], bv[t & 1]);
       if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
       else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
-      issue_codes(code_step, t);
-      if (t == 3) issue_scales(sc_chunk, part % 4);
-      if (t < 3) interleave(NV2());
-      else interleave(NV4());
+#pragma unroll
+      for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(code_step, q);
+      if (t == 3) issue_scales(sc_chunk, (part % 4) % TA, part % 4);
+      if (t == 0) interleave(std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
+      if (t == 1) interleave(std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
+      if (t == 2) interleave(std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
+      if (t == 3) interleave(std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
     }
-    wait_vm<10>();
+    wait_vm<TN + 2>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -676,7 +760,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         pairs(na, nb, npa, npb);
         decode_step(0, fa, fb, npa, npb, av[0], bv[0]);
       }
-      interleave(NV0());
+      interleave(std::integral_constant<int, 0>());
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -694,40 +778,50 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   asm volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
-  const float out_scale = (*p.a_g) * (*p.b_g);
-  constexpr int ROW_ELEMS = WN;
-  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;
+  // Each wave stages one 32-row slab (its fragment row i) at a time in its own
+  // LDS region, then writes it out row by row.  Accumulator register r of lane
+  // (l32, lh) in a 32x32 tile holds row 8*(r/4) + 4*lh + (r%4), column l32.
+  constexpr int ROW_ELEMS = WN_OUT;
+  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;  // +16: bank spread
   static_assert(4 * 32 * ROW_BYTES <= OFF_SC, "epilogue staging must fit");
   OutT *C = static_cast<OutT *>(p.c);
   uint8_t *slab = smem + wave * 32 * ROW_BYTES;
-  const uint32_t col0 = col0n + wn * WN;
+  const uint32_t col0 = tile_n * BN_OUT + wn * WN_OUT;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4);
       OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
+      if (SILU) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+        for (int j = 0; j < HALF; ++j)
+          dst[j * 32 + l32] =
+              to_out<OutT>(silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale));
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
+    // 32 rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
     constexpr int VEC = 16 / (int)sizeof(OutT);
-    constexpr int CPR = ROW_ELEMS / VEC;
+    constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
     const uint32_t rbase = row0 + wm * WM + i * 32;
     for (int c = lane; c < 32 * CPR; c += 64) {
       const uint32_t tr = c / CPR, cc = c % CPR;
       const uint32_t row = rbase + tr;
       const uint32_t col = col0 + cc * VEC;
-      if (row >= p.M) continue;
+      if (row >= row_end) continue;
       const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
       OutT *g = C + (int64_t)row * p.ldc + col;
-      if (VSTORE && col + VEC <= p.N) {
+      if (VSTORE && col + VEC <= n_out) {
         *reinterpret_cast<u32x4 *>(g) = *reinterpret_cast<const u32x4 *>(srcp);
       } else {
         const OutT *sv = reinterpret_cast<const OutT *>(srcp);
         for (int e = 0; e < VEC; ++e)
-          if (col + e < p.N) g[e] = sv[e];
+          if (col + e < n_out) g[e] = sv[e];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -755,6 +849,53 @@ bool operands_aligned(const GemmParams &p) {
          p.b_mstride_q % 16 == 0 && p.b_mstride_s % 8 == 0;
 }
 
+// The direct-to-LDS kernel needs whole 256-element K chunks and per-lane byte
+// offsets that fit 32 bits (rows x K/2 for the codes of either operand).
+bool dma_ok(const GemmParams &p, uint64_t a_rows) {
+  const uint64_t kb = p.K / 2;
+  return p.K % 256 == 0 && a_rows * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32);
+}
+
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT>
+hipError_t launch_dma(const GemmParams &p, uint32_t grid, hipStream_t stream) {
+  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Tile height for the grouped GEMM from the mean rows per expert m = R / E.
+// Per-expert counts of a top-k router spread like a Poisson count around m,
+// and an expert with n rows costs ceil(n / BM) tiles of BM rows.  Shorter
+// tiles waste fewer rows but cost more per row: the wave tile is BM/2 x 128,
+// so the decode work per MFMA grows as BM shrinks, and a K step has fewer
+// MFMAs to hide it under.  Relative cost per computed row, measured on MI355X
+// with this kernel: 1.5 (128 rows), 1.2 (192), 1.0 (256).  The expected cost
+// of each height is estimated over 32 quantiles of a normal N(m, m) and the
+// cheapest height wins.
+int grouped_tile_rows(uint32_t R, uint32_t E) {
+  const double m = (double)R / (double)E, sd = m > 1.0 ? __builtin_sqrt(m) : 1.0;
+  // upper half of the standard normal quantiles at (i + 0.5) / 32
+  static const double z[16] = {0.0392, 0.1178, 0.1971, 0.2777, 0.3601, 0.4451, 0.5334, 0.6261,
+                               0.7245, 0.8305, 0.9468, 1.0775, 1.2299, 1.4178, 1.6759, 2.1539};
+  static const int height[3] = {128, 192, 256};
+  static const double row_cost[3] = {1.5, 1.2, 1.0};
+  int best = 128;
+  double best_cost = 1e300;
+  for (int h = 0; h < 3; ++h) {
+    double tiles = 0.0;
+    for (int i = 0; i < 16; ++i)
+      for (int sgn = -1; sgn <= 1; sgn += 2) {
+        const double n = m + sgn * z[i] * sd;
+        tiles += n > 0.0 ? __builtin_ceil(n / height[h]) : 0.0;
+      }
+    const double cost = tiles / 32.0 * height[h] * row_cost[h];
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = height[h];
+    }
+  }
+  return best;
+}
+
 bool stores_aligned(const GemmParams &p, OutType out) {
   const int64_t es = out == OutType::BF16 ? 2 : 4;
   return ((uintptr_t)p.c & 15u) == 0 && (p.ldc * es) % 16 == 0;
@@ -767,17 +908,12 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
   constexpr int BM = 256, BN = 256;
   const uint32_t grid = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const bool al = operands_aligned(p), vs = stores_aligned(p, out);
-  const uint64_t kb = p.K / 2;
-  const bool fits32 = (uint64_t)p.M * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32);
-  if (al && fits32 && p.K % 256 == 0) {
-    if (out == OutType::BF16) {
-      if (vs) gemm_dma_kernel<true, uint16_t><<<grid, 256, 0, stream>>>(p);
-      else gemm_dma_kernel<false, uint16_t><<<grid, 256, 0, stream>>>(p);
-    } else {
-      if (vs) gemm_dma_kernel<true, float><<<grid, 256, 0, stream>>>(p);
-      else gemm_dma_kernel<false, float><<<grid, 256, 0, stream>>>(p);
-    }
-    return hipGetLastError();
+  if (al && dma_ok(p, p.M)) {
+    if (out == OutType::BF16)
+      return vs ? launch_dma<BM, false, false, true, uint16_t>(p, grid, stream)
+                : launch_dma<BM, false, false, false, uint16_t>(p, grid, stream);
+    return vs ? launch_dma<BM, false, false, true, float>(p, grid, stream)
+              : launch_dma<BM, false, false, false, float>(p, grid, stream);
   }
   return out == OutType::BF16
              ? launch_cfg<BM, BN, 128, 128, false, false, uint16_t>(p, grid, al, vs, stream)
@@ -787,15 +923,39 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
 hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epilogue epi,
                                hipStream_t stream) {
   if (R == 0) return hipSuccess;
-  constexpr int BM = 128, BN = 256;
+  constexpr int BN = 256;
   const bool silu = epi == Epilogue::SiluGate;
   const uint32_t n_out = silu ? p.N / 2 : p.N;
   const uint32_t bn_out = silu ? BN / 2 : BN;
   const uint32_t tiles_n = (n_out + bn_out - 1) / bn_out;
   // sum_e ceil(n_e / BM) <= R / BM + E
-  const uint64_t tiles_m = (uint64_t)(R + BM - 1) / BM + p.E;
-  const uint32_t grid = (uint32_t)(tiles_m * tiles_n);
+  auto grid_for = [&](uint32_t bm) {
+    return (uint32_t)(((uint64_t)(R + bm - 1) / bm + p.E) * tiles_n);
+  };
   const bool al = operands_aligned(p), vs = stores_aligned(p, out);
+  if (al && dma_ok(p, p.a_rows)) {
+    const int bm = grouped_tile_rows(R, p.E);
+    const uint32_t grid = grid_for((uint32_t)bm);
+    auto go = [&](auto bm_tag) -> hipError_t {
+      constexpr int TBM = decltype(bm_tag)::value;
+      if (silu)
+        return out == OutType::BF16
+                   ? (vs ? launch_dma<TBM, true, true, true, uint16_t>(p, grid, stream)
+                         : launch_dma<TBM, true, true, false, uint16_t>(p, grid, stream))
+                   : (vs ? launch_dma<TBM, true, true, true, float>(p, grid, stream)
+                         : launch_dma<TBM, true, true, false, float>(p, grid, stream));
+      return out == OutType::BF16
+                 ? (vs ? launch_dma<TBM, true, false, true, uint16_t>(p, grid, stream)
+                       : launch_dma<TBM, true, false, false, uint16_t>(p, grid, stream))
+                 : (vs ? launch_dma<TBM, true, false, true, float>(p, grid, stream)
+                       : launch_dma<TBM, true, false, false, float>(p, grid, stream));
+    };
+    if (bm == 256) return go(std::integral_constant<int, 256>());
+    if (bm == 192) return go(std::integral_constant<int, 192>());
+    return go(std::integral_constant<int, 128>());
+  }
+  constexpr int BM = 128;
+  const uint32_t grid = grid_for(BM);
   if (silu)
     return out == OutType::BF16
                ? launch_cfg<BM, BN, 64, 128, true, true, uint16_t>(p, grid, al, vs, stream)

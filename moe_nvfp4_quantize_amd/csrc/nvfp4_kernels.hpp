@@ -57,6 +57,7 @@ struct GemmParams {
   void *c;
   int64_t ldc;
   // grouped (MoE) mode
+  uint32_t a_rows;                // rows of A (the gather's source rows)
   const int32_t *src_row;         // nullable row gather
   const int32_t *expert_offsets;  // [E+1]
   uint32_t E;

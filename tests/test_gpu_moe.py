@@ -151,9 +151,12 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True):
     return out, offsets
 
 
+# Rows per expert decide the grouped kernel's tile height (128, 192 or 256
+# rows): about 60, 125, 150 and 1000 rows per expert below cover all three.
 @pytest.mark.parametrize("epi", [0, 1])
 @pytest.mark.parametrize("T,E,k,H,N", [(200, 7, 2, 256, 256), (37, 5, 3, 48, 96), (500, 16, 4, 512, 384),
-                                       (1, 4, 1, 256, 64)])
+                                       (1, 4, 1, 256, 64), (600, 4, 1, 512, 256),
+                                       (2000, 2, 1, 256, 512)])
 def test_grouped_gemm_small(B, T, E, k, H, N, epi):
     _grouped_case(B, T, E, k, H, N, epi, seed=T + E + N)
 
