@@ -478,21 +478,32 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   const uint32_t K = p.K, kbytes = K / 2, kscales = K / 16;
   const uint32_t n_out = SILU ? p.N / 2 : p.N;
   const uint32_t tiles_n = (n_out + BN_OUT - 1) / BN_OUT;
-  const uint32_t nsteps = K / 128;
+  const uint32_t nsteps = K / 128, cpt = (nsteps + SC_STEPS - 1) / SC_STEPS;
 
-  // ---------------------------------------------------------------- tile
-  uint32_t tile_n, row0, row_end;
+  // ---------------------------------------------------------------- tiles
+  // Dense: workgroup b computes tiles b, b + G, b + 2G, ... (G = gridDim.x, a
+  // multiple of 8, so they all map to the XCD of b; the host launches more
+  // than one tile per workgroup only when K % 1024 == 0).  Grouped: one tile.
+  uint32_t my_tiles, row0, row_end, tile_n;
   const uint8_t *bq = p.b_q, *bs = p.b_s;
   float b_g;
-  if (!GROUPED) {
-    const uint32_t tiles_m = (p.M + BM - 1) / BM;
+  uint32_t tiles_m = 0;
+  auto origin = [&](uint32_t i, uint32_t *r0, uint32_t *tn) {
     uint32_t tm;
-    dense_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tile_n);
-    row0 = tm * BM;
+    dense_tile(blockIdx.x + i * gridDim.x, tiles_m, tiles_n, &tm, tn);
+    *r0 = tm * BM;
+  };
+  if (!GROUPED) {
+    tiles_m = (p.M + BM - 1) / BM;
+    const uint32_t ntiles = tiles_m * tiles_n;
+    if (blockIdx.x >= ntiles) return;
+    my_tiles = (ntiles - 1 - blockIdx.x) / gridDim.x + 1;
+    origin(0, &row0, &tile_n);
     row_end = p.M;
     b_g = *p.b_g;
   } else {
     // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM)
+    my_tiles = 1;
     tile_n = blockIdx.x % tiles_n;
     const uint32_t tile_mm = blockIdx.x / tiles_n;
     if (tid == 0) sInfo[0] = -1;
@@ -528,14 +539,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     bq += (int64_t)e * p.b_mstride_q;
     bs += (int64_t)e * p.b_mstride_s;
     b_g = p.b_g[e];
+    for (uint32_t r = tid; r < BM; r += 256) {
+      const uint32_t row = row0 + r;
+      int32_t src = -1;
+      if (row < row_end) src = p.src_row ? p.src_row[row] : (int32_t)row;
+      sRow[r] = src;
+    }
   }
   const float out_scale = (*p.a_g) * b_g;
-  for (uint32_t r = tid; r < BM; r += 256) {
-    const uint32_t row = row0 + r;
-    int32_t src = -1;
-    if (row < row_end) src = (GROUPED && p.src_row) ? p.src_row[row] : (int32_t)row;
-    sRow[r] = src;
-  }
   // B-tile row rho -> weight row (or -1 past N).  With SILU, in every wave the
   // first FN/2 fragments hold gate columns and the last FN/2 the matching up
   // columns (weight rows n and N/2 + n).
@@ -555,45 +566,75 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // Global -> LDS transfers.  One transfer moves 64 lanes x 16 bytes into 1 KB
   // of consecutive LDS: transfer j of an operand covers slots s = j * 256 + tid,
   // i.e. tile row s / 4, physical 16-byte piece s % 4, which holds logical
-  // piece (s % 4) ^ swz(row) = pc for every j.  Rows past the end read a valid
-  // row instead (results never stored).  Byte offsets from the operand bases
-  // fit 32 bits (checked by the host).
+  // piece (s % 4) ^ swz(row) = pc for every j.  A lane's byte offset is
+  // min(l + base, last): dense tiles keep the lane part l (row inside the
+  // tile) and add the tile's first row as a uniform base, clamped to the last
+  // row of the matrix (rows past the end are never stored); grouped tiles hold
+  // the full offset of the gathered row (base 0, no clamp).  Offsets fit 32
+  // bits (checked by the host).
   const uint32_t pc = (tid % 4) ^ swz(tid / 4);
-  u32x4 oa = {0, 0, 0, 0}, ob, osa = {0, 0, 0, 0}, osb;
-  const int32_t a_fallback = sRow[0];  // the tile's first row always exists
+  u32x4 la = {0, 0, 0, 0}, lb, lsa = {0, 0, 0, 0}, lsb;
+  uint32_t last_a, last_b, last_sa, last_sb;
+  if (!GROUPED) {
 #pragma unroll
-  for (int j = 0; j < TA; ++j) {
-    const int32_t src = sRow[j * 64 + tid / 4];
-    const uint32_t ra = GROUPED ? (uint32_t)(src >= 0 ? src : a_fallback)
-                                : min(row0 + j * 64 + tid / 4, p.M - 1);
-    oa[j] = ra * kbytes + pc * 16;
-    osa[j] = ra * kscales + pc * 16;
-  }
+    for (int j = 0; j < TA; ++j) {
+      la[j] = (j * 64 + tid / 4) * kbytes + pc * 16;
+      lsa[j] = (j * 64 + tid / 4) * kscales + pc * 16;
+    }
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int32_t w = b_row(j * 64 + tid / 4);
-    const uint32_t rb = (uint32_t)(w >= 0 ? w : 0);
-    ob[j] = rb * kbytes + pc * 16;
-    osb[j] = rb * kscales + pc * 16;
+    for (int j = 0; j < TB; ++j) {
+      lb[j] = (j * 64 + tid / 4) * kbytes + pc * 16;
+      lsb[j] = (j * 64 + tid / 4) * kscales + pc * 16;
+    }
+    last_a = (p.M - 1) * kbytes + pc * 16;
+    last_sa = (p.M - 1) * kscales + pc * 16;
+    last_b = (p.N - 1) * kbytes + pc * 16;
+    last_sb = (p.N - 1) * kscales + pc * 16;
+  } else {
+    const int32_t a_fallback = sRow[0];  // the tile's first row always exists
+#pragma unroll
+    for (int j = 0; j < TA; ++j) {
+      const int32_t src = sRow[j * 64 + tid / 4];
+      const uint32_t ra = (uint32_t)(src >= 0 ? src : a_fallback);
+      la[j] = ra * kbytes + pc * 16;
+      lsa[j] = ra * kscales + pc * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int32_t w = b_row(j * 64 + tid / 4);
+      const uint32_t rb = (uint32_t)(w >= 0 ? w : 0);
+      lb[j] = rb * kbytes + pc * 16;
+      lsb[j] = rb * kscales + pc * 16;
+    }
+    last_a = last_b = last_sa = last_sb = 0xFFFFFFFFu;
   }
   __syncthreads();  // every wave is done with the set-up tables
-  // code transfer q (0 .. TN - 1; A first) of step ks
-  auto issue_code = [&](uint32_t ks, int q) {
-    uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
-    if (q < TA)
-      __builtin_amdgcn_global_load_lds((glb_void *)(p.a_q + ks * 64 + oa[q]), (lds_void *)(st + q * 4096 + wave * 1024), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + ob[q - TA]), (lds_void *)(st + CODE_B + (q - TA) * 4096 + wave * 1024), 16, 0, 0);
+  // first A row and first B row of a tile as used in the offsets (0 when grouped)
+  auto a_base = [&](uint32_t r0) { return GROUPED ? 0u : r0; };
+  auto b_base = [&](uint32_t tn) { return GROUPED ? 0u : tn * BN; };
+  // code transfer q (0 .. TN - 1; A first) of K step ks of the tile at (ar, bc),
+  // into the stage of global step g
+  auto issue_code = [&](uint32_t g, uint32_t ks, uint32_t ar, uint32_t bc, int q) {
+    uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
+    if (q < TA) {
+      const uint32_t off = min(la[q] + ar * kbytes, last_a);
+      __builtin_amdgcn_global_load_lds((glb_void *)(p.a_q + ks * 64 + off), (lds_void *)(st + q * 4096 + wave * 1024), 16, 0, 0);
+    } else {
+      const uint32_t off = min(lb[q - TA] + bc * kbytes, last_b);
+      __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + off), (lds_void *)(st + CODE_B + (q - TA) * 4096 + wave * 1024), 16, 0, 0);
+    }
   };
-  // scale transfers of chunk c: A transfer ja and B transfer jb (both possibly
-  // not known at compile time: vector selects, no indexing into memory).  A
-  // piece past the end of the row reloads the chunk's first piece instead
-  // (K % 256 == 0 keeps that in the row).
-  auto issue_scales = [&](uint32_t c, uint32_t ja, uint32_t jb) {
-    uint8_t *st = smem + OFF_SC + (c % 2) * SC_CHUNK + wave * 1024;
+  // scale transfers of chunk c of the tile at (ar, bc), into the buffer of
+  // global chunk gc: A transfer ja and B transfer jb (possibly not known at
+  // compile time: vector selects, no indexing into memory).  A piece past the
+  // end of the row reloads the chunk's first piece instead (K % 256 == 0
+  // keeps that in the row).
+  auto issue_scales = [&](uint32_t gc, uint32_t c, uint32_t ar, uint32_t bc, uint32_t ja, uint32_t jb) {
+    uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + wave * 1024;
     const uint32_t back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16;
-    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + osa[ja] - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + osb[jb] - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
+    const uint32_t oa = min(lsa[ja] + ar * kscales, last_sa), ob = min(lsb[jb] + bc * kscales, last_sb);
+    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + oa - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
   };
 
   const uint32_t wm = wave / 2, wn = wave % 2;
@@ -626,18 +667,18 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4 fa[FM], fb[FN];
-  uint32_t sa[FM], sb[FN];
-  auto read_half = [&](uint32_t ks, int h, u32x4 *xa, u32x4 *xb) {
-    const uint8_t *st = smem + (ks % NSTAGE) * CODE_STAGE;
+  // fragments of half h of the code stage of global step g
+  auto read_half = [&](uint32_t g, int h, u32x4 *xa, u32x4 *xb) {
+    const uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
 #pragma unroll
     for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
   };
-  // scale dword of step ks: piece (ks % 8) / 2 of the row's 64 bytes, half ks % 2
-  auto read_scales = [&](uint32_t ks, uint32_t *xa, uint32_t *xb) {
-    const uint8_t *st = smem + OFF_SC + ((ks / SC_STEPS) % 2) * SC_CHUNK + (ks % 2) * 8;
+  // scale dword of K step ks held in global chunk gc: piece (ks % 8) / 2 of
+  // the row's 64 bytes, half ks % 2
+  auto read_scales = [&](uint32_t gc, uint32_t ks, uint32_t *xa, uint32_t *xb) {
+    const uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + (ks % 2) * 8;
     const uint32_t q = (ks % SC_STEPS) / 2;
 #pragma unroll
     for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
@@ -687,144 +728,199 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // code transfers placed in MFMA sub-step t (0..3) of the first half
-  auto codes_in = [](int t) { return ((t + 1) * TN + 3) / 4 - (t * TN + 3) / 4; };
-
-  // ---------------------------------------------------------------- K loop
-  // Software pipeline: while the MFMAs of sub-step t run, the operands of
-  // sub-step t + 1 are decoded; the next K step's first half is read from LDS
-  // while this step's second half is multiplied.  Codes are fetched two K
-  // steps ahead; scale chunk c + 1 during the first four steps of chunk c.
-  // Every step issues TN + 2 transfers (near the end the last step's codes
-  // again, into a stage nobody reads any more; outside the first four steps of
-  // a chunk the current chunk's scales again, rewriting identical bytes), so
-  // at the mid-step barrier one wait count leaves exactly this step's own
-  // transfers in flight.
-#pragma unroll
-  for (int j = 0; j < 4; ++j) issue_scales(0, j % TA, j);
-#pragma unroll
-  for (int q = 0; q < TN; ++q) issue_code(0, q);
-#pragma unroll
-  for (int q = 0; q < TN; ++q) issue_code(min(1u, nsteps - 1), q);
-  wait_vm<TN>();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  read_half(0, 0, fa, fb);
-  read_scales(0, sa, sb);
-  wait_lgkm0();
-  half2v spa[FM][2], spb[FN][2];
-  pairs(sa, sb, spa, spb);
-  half8v av[2][FM], bv[2][FN];
-  decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
-  for (uint32_t ks = 0; ks < nsteps; ++ks) {
-    const uint32_t code_step = min(ks + 2, nsteps - 1);
-    const uint32_t part = ks % SC_STEPS, chunk = ks / SC_STEPS;
-    const uint32_t sc_chunk = (part < 4 && (chunk + 1) * SC_STEPS < nsteps) ? chunk + 1 : chunk;
-    u32x4 ha[FM], hb[FN];
-    read_half(ks, 1, ha, hb);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      mfmas(av[t & 1], bv[t & 1]);
-      if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
-      else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
-#pragma unroll
-      for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(code_step, q);
-      if (t == 3) issue_scales(sc_chunk, (part % 4) % TA, part % 4);
-      if (t == 0) interleave(std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
-      if (t == 1) interleave(std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
-      if (t == 2) interleave(std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
-      if (t == 3) interleave(std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
-    }
-    wait_vm<TN + 2>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // the next step's first half (at the last step: stale data, never used)
-    uint32_t na[FM], nb[FN];
-    read_half(ks + 1, 0, fa, fb);
-    read_scales(ks + 1, na, nb);
-    __builtin_amdgcn_sched_barrier(0);
-    half2v npa[FM][2], npb[FN][2];
-#pragma unroll
-    for (int t = 4; t < 8; ++t) {
-      mfmas(av[t & 1], bv[t & 1]);
-      if (t < 7) {
-        decode_step(t + 1, ha, hb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
-      } else {
-        // keep the next step's operands from being used (and waited for) earlier
-#pragma unroll
-        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
-#pragma unroll
-        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
-        pairs(na, nb, npa, npb);
-        decode_step(0, fa, fb, npa, npb, av[0], bv[0]);
-      }
-      interleave(std::integral_constant<int, 0>());
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      spa[i][0] = npa[i][0];
-      spa[i][1] = npa[i][1];
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      spb[j][0] = npb[j][0];
-      spb[j][1] = npb[j][1];
-    }
-  }
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
-  // Each wave stages one 32-row slab (its fragment row i) at a time in its own
-  // LDS region, then writes it out row by row.  Accumulator register r of lane
-  // (l32, lh) in a 32x32 tile holds row 8*(r/4) + 4*lh + (r%4), column l32.
+  // Each wave stages RPP rows of one fragment row i at a time in its own part
+  // of the code stage of the tile's last K step (free from the mid-step
+  // barrier of that step until the next step's transfers, which a workgroup
+  // barrier after the epilogue holds back), then writes them out 16 bytes per
+  // lane.  Accumulator register r of lane (l32, lh) in a 32x32 tile holds row
+  // 8*(r/4) + 4*lh + (r%4), column l32.
   constexpr int ROW_ELEMS = WN_OUT;
   constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;  // +16: bank spread
-  static_assert(4 * 32 * ROW_BYTES <= OFF_SC, "epilogue staging must fit");
+  constexpr int RPP = 4 * 16 * ROW_BYTES <= CODE_STAGE ? 16 : 8;  // rows per pass
+  static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
-  uint8_t *slab = smem + wave * 32 * ROW_BYTES;
-  const uint32_t col0 = tile_n * BN_OUT + wn * WN_OUT;
+  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn) {
+    uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
+    const uint32_t col0 = tn * BN_OUT + wn * WN_OUT;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4);
-      OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
-      if (SILU) {
+      for (int ps = 0; ps < 32 / RPP; ++ps) {
 #pragma unroll
-        for (int j = 0; j < HALF; ++j)
-          dst[j * 32 + l32] =
-              to_out<OutT>(silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale));
-      } else {
+        for (int r = ps * (RPP / 2); r < (ps + 1) * (RPP / 2); ++r) {
+          // one accumulator register at a time: the tile's live pipeline state
+          // leaves few free registers here
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4) - ps * RPP;
+          OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
+          if (SILU) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+            for (int j = 0; j < HALF; ++j)
+              dst[j * 32 + l32] =
+                  to_out<OutT>(silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale));
+          } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
+        constexpr int VEC = 16 / (int)sizeof(OutT);
+        constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
+        const uint32_t rbase = r0 + wm * WM + i * 32 + ps * RPP;
+        for (int c = lane; c < RPP * CPR; c += 64) {
+          const uint32_t tr = c / CPR, cc = c % CPR;
+          const uint32_t row = rbase + tr;
+          const uint32_t col = col0 + cc * VEC;
+          if (row >= row_end) continue;
+          const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
+          OutT *gp = C + (int64_t)row * p.ldc + col;
+          if (VSTORE && col + VEC <= n_out) {
+            *reinterpret_cast<u32x4 *>(gp) = *reinterpret_cast<const u32x4 *>(srcp);
+          } else {
+            const OutT *sv = reinterpret_cast<const OutT *>(srcp);
+            for (int e = 0; e < VEC; ++e)
+              if (col + e < n_out) gp[e] = sv[e];
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    // 32 rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
-    constexpr int VEC = 16 / (int)sizeof(OutT);
-    constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
-    const uint32_t rbase = row0 + wm * WM + i * 32;
-    for (int c = lane; c < 32 * CPR; c += 64) {
-      const uint32_t tr = c / CPR, cc = c % CPR;
-      const uint32_t row = rbase + tr;
-      const uint32_t col = col0 + cc * VEC;
-      if (row >= row_end) continue;
-      const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
-      OutT *g = C + (int64_t)row * p.ldc + col;
-      if (VSTORE && col + VEC <= n_out) {
-        *reinterpret_cast<u32x4 *>(g) = *reinterpret_cast<const u32x4 *>(srcp);
-      } else {
-        const OutT *sv = reinterpret_cast<const OutT *>(srcp);
-        for (int e = 0; e < VEC; ++e)
-          if (col + e < n_out) g[e] = sv[e];
+  };
+
+  // ---------------------------------------------------------------- K loop
+  // One stream of K steps over all tiles of the workgroup: global step g is K
+  // step ks of tile i.  Software pipeline: while the MFMAs of sub-step t run,
+  // the operands of sub-step t + 1 are decoded; the next step's first half is
+  // read from LDS while this step's second half is multiplied.  Codes are
+  // fetched two steps ahead (across a tile boundary: the next tile's first
+  // steps); scale chunk c + 1 (or the next tile's chunk 0) during the first
+  // four steps of chunk c.  Every step issues TN + 2 transfers (near the end
+  // the last step's codes again, into a stage nobody reads any more; outside
+  // the first four steps of a chunk the current chunk's scales again,
+  // rewriting identical bytes), so at the mid-step barrier one wait count
+  // leaves exactly this step's own transfers in flight.  At the last step of a
+  // tile its epilogue runs, behind the already issued transfers of the next.
+  uint32_t nrow0 = row0, ntile_n = tile_n;  // the tile after the current one
+  if (my_tiles > 1) origin(1, &nrow0, &ntile_n);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j % TA, j);
+#pragma unroll
+  for (int q = 0; q < TN; ++q) issue_code(0, 0, a_base(row0), b_base(tile_n), q);
+#pragma unroll
+  for (int q = 0; q < TN; ++q) issue_code(1, 1, a_base(row0), b_base(tile_n), q);
+  wait_vm<TN>();
+  uint32_t g = 0;
+  for (uint32_t ti = 0; ti < my_tiles; ++ti) {
+    // the tile's first step: its data landed before the previous barrier
+    // (fetched during the previous tile), or just above
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    u32x4 fa[FM], fb[FN];
+    uint32_t sa[FM], sb[FN];
+    read_half(g, 0, fa, fb);
+    read_scales(ti * cpt, 0, sa, sb);
+    wait_lgkm0();
+    half2v spa[FM][2], spb[FN][2];
+    pairs(sa, sb, spa, spb);
+    half8v av[2][FM], bv[2][FN];
+    decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
+    for (uint32_t ks = 0; ks < nsteps; ++ks, ++g) {
+      // codes of global step g + 2
+      uint32_t fks = ks + 2, far_ = a_base(row0), fbc = b_base(tile_n);
+      if (fks >= nsteps) {
+        if (ti + 1 < my_tiles) {
+          fks -= nsteps;
+          far_ = a_base(nrow0);
+          fbc = b_base(ntile_n);
+        } else {
+          fks = nsteps - 1;
+        }
+      }
+      // scale chunk: the next one during the first four steps of a chunk
+      const uint32_t part = ks % SC_STEPS, chunk = ks / SC_STEPS, gchunk = ti * cpt + chunk;
+      uint32_t sc_g = gchunk, sc_c = chunk, sar = a_base(row0), sbc = b_base(tile_n);
+      if (part < 4) {
+        if (chunk + 1 < cpt) {
+          sc_g = gchunk + 1;
+          sc_c = chunk + 1;
+        } else if (ti + 1 < my_tiles) {
+          sc_g = gchunk + 1;
+          sc_c = 0;
+          sar = a_base(nrow0);
+          sbc = b_base(ntile_n);
+        }
+      }
+      u32x4 ha[FM], hb[FN];
+      read_half(g, 1, ha, hb);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        mfmas(av[t & 1], bv[t & 1]);
+        if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+        else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
+#pragma unroll
+        for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + 2, fks, far_, fbc, q);
+        if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, (part % 4) % TA, part % 4);
+        if (t == 0) interleave(std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
+        if (t == 1) interleave(std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
+        if (t == 2) interleave(std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
+        if (t == 3) interleave(std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
+      }
+      wait_vm<TN + 2>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // the next step's first half (at a tile's last step: not used)
+      const uint32_t nks = ks + 1 < nsteps ? ks + 1 : 0;
+      uint32_t na[FM], nb[FN];
+      read_half(g + 1, 0, fa, fb);
+      read_scales(ti * cpt + nks / SC_STEPS, nks, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
+      half2v npa[FM][2], npb[FN][2];
+#pragma unroll
+      for (int t = 4; t < 8; ++t) {
+        mfmas(av[t & 1], bv[t & 1]);
+        if (t < 7) {
+          decode_step(t + 1, ha, hb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+        } else {
+          // keep the next step's operands from being used (and waited for) earlier
+#pragma unroll
+          for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
+#pragma unroll
+          for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
+          pairs(na, nb, npa, npb);
+          decode_step(0, fa, fb, npa, npb, av[0], bv[0]);
+        }
+        interleave(std::integral_constant<int, 0>());
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        spa[i][0] = npa[i][0];
+        spa[i][1] = npa[i][1];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        spb[j][0] = npb[j][0];
+        spb[j][1] = npb[j][1];
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    // the tile is done: the next tile's first steps are already in flight
+    wait_lgkm0();
+    epilogue(g - 1, row0, tile_n);
+    __syncthreads();  // staging done before the next step's transfers
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    row0 = nrow0;
+    tile_n = ntile_n;
+    if (ti + 2 < my_tiles) origin(ti + 2, &nrow0, &ntile_n);
   }
 }
 
@@ -854,6 +950,26 @@ bool operands_aligned(const GemmParams &p) {
 bool dma_ok(const GemmParams &p, uint64_t a_rows) {
   const uint64_t kb = p.K / 2;
   return p.K % 256 == 0 && a_rows * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32);
+}
+
+// Dense launches with whole 8-step scale chunks (K % 1024 == 0) run one
+// workgroup per compute unit, each walking its tiles with the next tile's
+// first K steps fetched during the current tile's last ones; otherwise one
+// workgroup per tile.  The CU count is a multiple of 8, which keeps every
+// workgroup's tiles on one XCD.
+uint32_t persistent_grid(const GemmParams &p, uint32_t tiles) {
+  if ((p.K / 128) % 8 != 0) return tiles;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return tiles;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return tiles;
+    cus[dev] = n;
+  }
+  const uint32_t g = (uint32_t)cus[dev] & ~7u;
+  return g == 0 || tiles <= g ? tiles : g;
 }
 
 template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT>
@@ -909,11 +1025,19 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
   const uint32_t grid = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const bool al = operands_aligned(p), vs = stores_aligned(p, out);
   if (al && dma_ok(p, p.M)) {
-    if (out == OutType::BF16)
-      return vs ? launch_dma<BM, false, false, true, uint16_t>(p, grid, stream)
-                : launch_dma<BM, false, false, false, uint16_t>(p, grid, stream);
-    return vs ? launch_dma<BM, false, false, true, float>(p, grid, stream)
-              : launch_dma<BM, false, false, false, float>(p, grid, stream);
+    // skinny products (decode batches, lm_head) take the 128-row tile: half the
+    // MFMA work of a mostly empty 256-row tile, twice the workgroups
+    auto go = [&](auto bm_tag) -> hipError_t {
+      constexpr int TBM = decltype(bm_tag)::value;
+      const uint32_t tiles = ((p.N + BN - 1) / BN) * ((p.M + TBM - 1) / TBM);
+      const uint32_t g = persistent_grid(p, tiles);
+      if (out == OutType::BF16)
+        return vs ? launch_dma<TBM, false, false, true, uint16_t>(p, g, stream)
+                  : launch_dma<TBM, false, false, false, uint16_t>(p, g, stream);
+      return vs ? launch_dma<TBM, false, false, true, float>(p, g, stream)
+                : launch_dma<TBM, false, false, false, float>(p, g, stream);
+    };
+    return p.M <= 128 ? go(std::integral_constant<int, 128>()) : go(std::integral_constant<int, BM>());
   }
   return out == OutType::BF16
              ? launch_cfg<BM, BN, 128, 128, false, false, uint16_t>(p, grid, al, vs, stream)

@@ -114,7 +114,7 @@ def test_every_code_and_scale_decodes_exactly(B):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (37, 200, 272), (130, 129, 512), (5, 300, 48),
-                                   (256, 256, 768), (129, 1, 4096)])
+                                   (256, 256, 768), (129, 1, 4096), (100, 300, 512), (1, 513, 256)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_ragged_shapes(B, M, N, K, out_dtype):
     rng = np.random.default_rng(M * N + K)
