@@ -194,6 +194,36 @@ nvfp4_status nvfp4_moe_grouped_gemm(
     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped gate_up GEMM with the SiLU-gate epilogue writing h directly as
+ * NVFP4 under a static (calibrated) global scale.  The two-level scaling page
+ * calibrates activations with a max over sampled batches (sub-section "The
+ * A4 side: dynamic activations"), and its checkpoint audit lists two FP32
+ * values per quantized tensor, read here as the weight's global scale and a
+ * calibrated activation scale.  With the activation scale known, the down
+ * projection's input needs no pass of its own: h = SiLU(gate) * up is
+ * quantized in the epilogue of the GEMM that produces it.
+ *
+ * Same operands and expert segments as nvfp4_moe_grouped_gemm with
+ * NVFP4_EPI_SILU_GATE (N = 2I, gate rows [0, I), up rows [I, 2I)); h[r][i] is
+ * computed in float32 exactly as that call would return it with c_type
+ * NVFP4_F32, then quantized block by block as nvfp4_quantize does with
+ * static_global != 0:
+ * h_q     uint8 [R][I/2]   codes of h (rows past offsets[E] not written)
+ * h_s     uint8 [R][I/16]  E4M3 block scales
+ * h_g     device float [1], read: the static global scale of h (a positive
+ *         normal float >= 2^-100; values beyond 6*448*h_g saturate)
+ * I = N/2 must be a multiple of 16.  This fused path needs K % 256 == 0,
+ * a_q, a_s, w_q, w_s 16-byte aligned and h_q 8-byte aligned; other valid
+ * requests return NVFP4_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_moe_grouped_gemm_silu_nvfp4(
+    const uint8_t *a_q, const uint8_t *a_s, const float *a_g, int64_t a_rows,
+    const int32_t *src_row, const int32_t *expert_offsets, int32_t E, int64_t R,
+    const uint8_t *w_q, const uint8_t *w_s, const float *w_g, int64_t N,
+    int64_t K, uint8_t *h_q, uint8_t *h_s, const float *h_g,
+    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Weighted unpermute (combine) of routed-row outputs back to tokens:
  *   out[t][h] = sum_{j=0..k-1} topk_w[t][j] * y[inv[t][j]][h]
  * summed in float32 in slot order, rounded to out_type.

@@ -218,6 +218,39 @@ nvfp4_status nvfp4_moe_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, cons
       epilogue == NVFP4_EPI_SILU_GATE ? Epilogue::SiluGate : Epilogue::None, stream));
 }
 
+nvfp4_status nvfp4_moe_grouped_gemm_silu_nvfp4(
+    const uint8_t *a_q, const uint8_t *a_s, const float *a_g, int64_t a_rows,
+    const int32_t *src_row, const int32_t *expert_offsets, int32_t E, int64_t R,
+    const uint8_t *w_q, const uint8_t *w_s, const float *w_g, int64_t N, int64_t K, uint8_t *h_q,
+    uint8_t *h_s, const float *h_g, hipStream_t stream) {
+  if (E < 1 || R < 0 || N <= 0 || K <= 0 || K % 16 != 0 || a_rows < 0 || N % 32 != 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (R > kI32Max || N > kI32Max || K > kI32Max || a_rows > kI32Max || E > 65536)
+    return NVFP4_ERR_INVALID_ARG;
+  if (R == 0) return NVFP4_OK;
+  if (!a_q || !a_s || !a_g || !expert_offsets || !w_q || !w_s || !w_g || !h_q || !h_s || !h_g ||
+      a_rows == 0)
+    return NVFP4_ERR_INVALID_ARG;
+  if (!src_row && a_rows < R) return NVFP4_ERR_INVALID_ARG;
+  GemmParams p{};
+  p.a_q = a_q; p.a_s = a_s; p.a_g = a_g;
+  p.b_q = w_q; p.b_s = w_s; p.b_g = w_g;
+  p.M = (uint32_t)R; p.N = (uint32_t)N; p.K = (uint32_t)K;
+  p.c = nullptr;
+  p.ldc = N / 2;
+  p.a_rows = (uint32_t)a_rows;
+  p.src_row = src_row;
+  p.expert_offsets = expert_offsets;
+  p.E = (uint32_t)E;
+  p.b_mstride_q = N * (K / 2);
+  p.b_mstride_s = N * (K / 16);
+  p.h_q = h_q; p.h_s = h_s; p.h_g = h_g;
+  if (!grouped_nvfp4_out_supported(p)) return NVFP4_ERR_UNSUPPORTED;
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  return from_hip(launch_grouped_gemm(p, (uint32_t)R, OutType::F32, Epilogue::SiluGateNvfp4, stream));
+}
+
 nvfp4_status nvfp4_moe_combine(const void *y, nvfp4_dtype y_type, const float *topk_w,
                                const int32_t *inv, int64_t T, int32_t k, int64_t H, int64_t R,
                                void *out, nvfp4_dtype out_type, hipStream_t stream) {

@@ -452,11 +452,12 @@ __device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
 //  * Decode is software pipelined: while the 16 MFMAs of sub-step t run, the
 //    operands of sub-step t + 1 are decoded (one MFMA, then four VALU
 //    instructions, sixteen times).
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr int BN = 256, WM = BM / 2, WN = 128, FM = WM / 32, FN = 4, HALF = FN / 2;
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile height");
   static_assert(!SILU || GROUPED, "the SiLU epilogue is a grouped-GEMM epilogue");
+  static_assert(!QOUT || (SILU && sizeof(OutT) == 4), "NVFP4 output: SiLU-gate epilogue, f32 staging");
   // transfers (64 lanes x 16 bytes) per operand: per code stage, and per scale chunk
   constexpr int TA = BM / 64, TB = BN / 64, TN = TA + TB;
   // code stages: [A BM rows x 64 B][B 256 rows x 64 B], three of them
@@ -547,6 +548,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     }
   }
   const float out_scale = (*p.a_g) * b_g;
+  // static global scale of an NVFP4 output (QOUT)
+  const float h_g = QOUT ? *p.h_g : 1.0f;
+  const float h_six_g = 6.0f * h_g, h_inv_six_g = 1.0f / h_six_g;
   // B-tile row rho -> weight row (or -1 past N).  With SILU, in every wave the
   // first FN/2 fragments hold gate columns and the last FN/2 the matching up
   // columns (weight rows n and N/2 + n).
@@ -767,10 +771,48 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
+        const uint32_t rbase = r0 + wm * WM + i * 32 + ps * RPP;
+        if constexpr (QOUT) {
+          // NVFP4 output with the static global scale: one 16-element block per
+          // lane (RPP rows x ROW_ELEMS / 16 blocks), the quantizer's arithmetic
+          static_assert(RPP * (ROW_ELEMS / 16) == 64, "one block per lane");
+          const uint32_t tr = lane / (ROW_ELEMS / 16), bk = lane % (ROW_ELEMS / 16);
+          const uint32_t row = rbase + tr, col = col0 + bk * 16;
+          if (row < row_end && col < n_out) {
+            const u32x4 *hv = reinterpret_cast<const u32x4 *>(slab + tr * ROW_BYTES + bk * 64);
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const u32x4 t = hv[k];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[4 * k + e] = u2f(t[e]);  // (by value: a bit cast
+                                                                     // of a vector element
+                                                                     // lvalue reads element 0)
+            }
+            float bmax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(v[e]));
+            const uint32_t sc = block_scale_code(bmax, h_six_g, h_inv_six_g);
+            const float rr = 1.0f / (e4m3_value(sc) * h_g);
+            uint32_t lo = 0, hi = 0;
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0] * rr, v[1] * rr, 1.0f, 0);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2] * rr, v[3] * rr, 1.0f, 1);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4] * rr, v[5] * rr, 1.0f, 2);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6] * rr, v[7] * rr, 1.0f, 3);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8] * rr, v[9] * rr, 1.0f, 0);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10] * rr, v[11] * rr, 1.0f, 1);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12] * rr, v[13] * rr, 1.0f, 2);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14] * rr, v[15] * rr, 1.0f, 3);
+            *reinterpret_cast<uint64_t *>(p.h_q + (int64_t)row * (n_out / 2) + col / 2) =
+                (uint64_t)lo | ((uint64_t)hi << 32);
+            p.h_s[(int64_t)row * (n_out / 16) + col / 16] = (uint8_t)sc;
+          }
+          __builtin_amdgcn_wave_barrier();
+          continue;
+        }
         // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
         constexpr int VEC = 16 / (int)sizeof(OutT);
         constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
-        const uint32_t rbase = r0 + wm * WM + i * 32 + ps * RPP;
         for (int c = lane; c < RPP * CPR; c += 64) {
           const uint32_t tr = c / CPR, cc = c % CPR;
           const uint32_t row = rbase + tr;
@@ -949,7 +991,10 @@ bool operands_aligned(const GemmParams &p) {
 // offsets that fit 32 bits (rows x K/2 for the codes of either operand).
 bool dma_ok(const GemmParams &p, uint64_t a_rows) {
   const uint64_t kb = p.K / 2;
-  return p.K % 256 == 0 && a_rows * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32);
+  auto al16 = [](const void *q) { return ((uintptr_t)q & 15u) == 0; };
+  return p.K % 256 == 0 && a_rows * kb < (1ull << 32) && (uint64_t)p.N * kb < (1ull << 32) &&
+         al16(p.a_q) && al16(p.a_s) && al16(p.b_q) && al16(p.b_s) && p.b_mstride_q % 16 == 0 &&
+         p.b_mstride_s % 16 == 0;
 }
 
 // Dense launches with whole 8-step scale chunks (K % 1024 == 0) run one
@@ -972,9 +1017,9 @@ uint32_t persistent_grid(const GemmParams &p, uint32_t tiles) {
   return g == 0 || tiles <= g ? tiles : g;
 }
 
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false>
 hipError_t launch_dma(const GemmParams &p, uint32_t grid, hipStream_t stream) {
-  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT><<<grid, 256, 0, stream>>>(p);
+  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT, QOUT><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -1019,6 +1064,11 @@ bool stores_aligned(const GemmParams &p, OutType out) {
 
 }  // namespace
 
+bool grouped_nvfp4_out_supported(const GemmParams &p) {
+  return operands_aligned(p) && dma_ok(p, p.a_rows) && (p.N / 2) % 16 == 0 &&
+         ((uintptr_t)p.h_q & 7u) == 0;
+}
+
 hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
   constexpr int BM = 256, BN = 256;
@@ -1048,7 +1098,7 @@ hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epi
                                hipStream_t stream) {
   if (R == 0) return hipSuccess;
   constexpr int BN = 256;
-  const bool silu = epi == Epilogue::SiluGate;
+  const bool silu = epi == Epilogue::SiluGate || epi == Epilogue::SiluGateNvfp4;
   const uint32_t n_out = silu ? p.N / 2 : p.N;
   const uint32_t bn_out = silu ? BN / 2 : BN;
   const uint32_t tiles_n = (n_out + bn_out - 1) / bn_out;
@@ -1057,11 +1107,14 @@ hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epi
     return (uint32_t)(((uint64_t)(R + bm - 1) / bm + p.E) * tiles_n);
   };
   const bool al = operands_aligned(p), vs = stores_aligned(p, out);
+  const bool qout = epi == Epilogue::SiluGateNvfp4;
+  if (qout && !(al && dma_ok(p, p.a_rows))) return hipErrorNotSupported;
   if (al && dma_ok(p, p.a_rows)) {
     const int bm = grouped_tile_rows(R, p.E);
     const uint32_t grid = grid_for((uint32_t)bm);
     auto go = [&](auto bm_tag) -> hipError_t {
       constexpr int TBM = decltype(bm_tag)::value;
+      if (qout) return launch_dma<TBM, true, true, false, float, true>(p, grid, stream);
       if (silu)
         return out == OutType::BF16
                    ? (vs ? launch_dma<TBM, true, true, true, uint16_t>(p, grid, stream)

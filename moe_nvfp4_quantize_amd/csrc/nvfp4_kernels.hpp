@@ -62,12 +62,17 @@ struct GemmParams {
   const int32_t *expert_offsets;  // [E+1]
   uint32_t E;
   int64_t b_mstride_q, b_mstride_s;  // bytes between expert matrices
+  // NVFP4 output of the SiLU-gate epilogue (static global scale h_g)
+  uint8_t *h_q, *h_s;
+  const float *h_g;
 };
 
 enum class OutType { F32, BF16 };
-enum class Epilogue { None, SiluGate };
+enum class Epilogue { None, SiluGate, SiluGateNvfp4 };
 
 hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream);
+// whether the fused SiLU-gate -> NVFP4 epilogue can run these operands
+bool grouped_nvfp4_out_supported(const GemmParams &p);
 hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epilogue epi,
                                hipStream_t stream);
 

@@ -45,6 +45,8 @@ SIGNATURES = {
     "nvfp4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_moe_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P,
                                               _I64, _I64, _P, ctypes.c_int, ctypes.c_int, _P]),
+    "nvfp4_moe_grouped_gemm_silu_nvfp4": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P,
+                                                         _P, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_moe_combine": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _I64, _I32, _I64, _I64, _P,
                                          ctypes.c_int, _P]),
 }
@@ -242,6 +244,30 @@ def nvfp4_moe_grouped_gemm(a, src_row, offsets, R, w, epilogue=NVFP4_EPI_NONE,
                                     _ptr(out), _dtype_code(out.dtype), epilogue, _stream(stream))
     _check("nvfp4_moe_grouped_gemm", st)
     return out
+
+
+def nvfp4_moe_grouped_gemm_silu_nvfp4(a, src_row, offsets, R, w, h_g, out=None, stream=None):
+    """Grouped gate_up GEMM whose SiLU-gate epilogue writes h = SiLU(gate) * up as NVFP4 under the
+    static global scale h_g (a one-element float32 device tensor).  Returns (h_q, h_s, h_g)."""
+    lib = load_library()
+    a_q, a_s, a_g = a
+    w_q, w_s, w_g = w
+    _on_gpu(a_q, a_s, a_g, src_row, offsets, w_q, w_s, w_g, h_g)
+    E, N, khalf = w_q.shape
+    K = khalf * 2
+    if a_q.shape[1] * 2 != K:
+        raise ValueError("K mismatch between activations and expert weights")
+    I = N // 2
+    if out is None:
+        out = (torch.empty((R, I // 2), dtype=torch.uint8, device=a_q.device),
+               torch.empty((R, I // 16), dtype=torch.uint8, device=a_q.device))
+    h_q, h_s = out
+    st = lib.nvfp4_moe_grouped_gemm_silu_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), a_q.shape[0],
+                                               _ptr(src_row), _ptr(offsets), E, R, _ptr(w_q),
+                                               _ptr(w_s), _ptr(w_g), N, K, _ptr(h_q), _ptr(h_s),
+                                               _ptr(h_g), _stream(stream))
+    _check("nvfp4_moe_grouped_gemm_silu_nvfp4", st)
+    return h_q, h_s, h_g
 
 
 def nvfp4_moe_combine(y, topk_w, inv, out_dtype=torch.bfloat16, out=None, stream=None):

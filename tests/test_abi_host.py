@@ -132,6 +132,23 @@ def test_grouped_gemm_rejects(lib):
     assert call(R=0, aq=None) == B.NVFP4_OK
 
 
+def test_grouped_silu_nvfp4_rejects(lib):
+    f = lib.nvfp4_moe_grouped_gemm_silu_nvfp4
+    ok = dict(aq=FAKE, as_=FAKE, ag=FAKE, arows=64, src=FAKE, off=FAKE, E=4, R=64, wq=FAKE, ws=FAKE,
+              wg=FAKE, N=64, K=256, hq=FAKE, hs=FAKE, hg=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["aq"], a["as_"], a["ag"], a["arows"], a["src"], a["off"], a["E"], a["R"], a["wq"],
+                 a["ws"], a["wg"], a["N"], a["K"], a["hq"], a["hs"], a["hg"], None)
+    for bad in [dict(K=8), dict(E=0), dict(N=0), dict(N=48), dict(R=-1), dict(hq=None),
+                dict(hs=None), dict(hg=None), dict(off=None), dict(src=None, arows=8), dict(arows=0)]:
+        assert call(**bad) == INVALID, bad
+    assert call(R=0, aq=None) == B.NVFP4_OK
+    # valid, but K % 256 != 0 is not implemented by the fused path
+    assert call(K=48) == B.NVFP4_ERR_UNSUPPORTED
+
+
 def test_combine_rejects(lib):
     f = lib.nvfp4_moe_combine
     ok = dict(y=FAKE, yt=B.NVFP4_F32, w=FAKE, inv=FAKE, T=4, k=2, H=16, R=8, out=FAKE,

@@ -178,6 +178,53 @@ def test_grouped_gemm_full_shapes_sampled(B, name, stage):
         _grouped_case(B, T, E, k, I, H, 0, seed=12, sample=sample, gather=False)
 
 
+# ------------------------------------------- fused SiLU-gate -> NVFP4 (static)
+
+
+@pytest.mark.parametrize("T,E,k,H,I,g_div", [(200, 7, 2, 256, 128, 1.0), (500, 16, 4, 512, 192, 1.0),
+                                             (600, 4, 1, 512, 128, 8.0), (2000, 2, 1, 256, 256, 1.0)])
+def test_gate_up_nvfp4_epilogue(B, T, E, k, H, I, g_div):
+    """The fused epilogue's h bytes equal the oracle's static quantization of the
+    unfused kernel's float32 h (same accumulation, so the same h), bit for bit.
+    g_div > 1 calibrates the scale below the batch's amax: saturated blocks."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(T * 7 + E)
+    logits = _routing(gen, T, E, k, dev, skew=True)
+    r = B.nvfp4_moe_route(logits, k)
+    R = T * k
+    a = _rand_nvfp4(gen, (T, H), dev)
+    w = _rand_nvfp4(gen, (E, 2 * I, H), dev)
+    h32 = B.nvfp4_moe_grouped_gemm(a, r["src_row"], r["offsets"], R, w,
+                                   epilogue=B.NVFP4_EPI_SILU_GATE, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    n = int(_np(r["offsets"])[-1])
+    h_np = _np(h32[:n]).astype(np.float32)
+    g_h = np.float32(OQ.global_scale(h_np) / np.float32(g_div))
+    hg = torch.tensor([float(g_h)], dtype=torch.float32, device=dev)
+    hq, hs, _ = B.nvfp4_moe_grouped_gemm_silu_nvfp4(a, r["src_row"], r["offsets"], R, w, hg)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = OQ.quantize(h_np, g=g_h)
+    np.testing.assert_array_equal(_np(hs[:n]), s_ref)
+    np.testing.assert_array_equal(_np(hq[:n]), q_ref)
+    print(f"[moe] fused gate_up NVFP4 T={T} E={E} I={I} g_div={g_div}: {n} rows bit-exact, "
+          f"{int((s_ref == 0x7E).sum())} blocks at scale 448", flush=True)
+
+
+def test_gate_up_nvfp4_epilogue_unsupported_layout(B):
+    # K % 256 != 0: the fused path reports "unsupported" instead of running
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    r = B.nvfp4_moe_route(_routing(gen, 40, 4, 2, dev), 2)
+    a = _rand_nvfp4(gen, (40, 48), dev)
+    w = _rand_nvfp4(gen, (4, 64, 48), dev)
+    hg = torch.ones(1, dtype=torch.float32, device=dev)
+    with pytest.raises(B.NVFP4Error) as ei:
+        B.nvfp4_moe_grouped_gemm_silu_nvfp4(a, r["src_row"], r["offsets"], 80, w, hg)
+    assert ei.value.status == B.NVFP4_ERR_UNSUPPORTED
+
+
 # ---------------------------------------------------------------- combine
 
 

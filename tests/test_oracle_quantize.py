@@ -183,8 +183,13 @@ def test_static_global_scale():
     q2, s2, g2 = Q.quantize(x)
     assert g1 == g2 and np.array_equal(q1, q2) and np.array_equal(s1, s2)
     # a global scale 4096x too small saturates: every non-zero block clamps to 448
-    q3, s3, _ = Q.quantize(x, g=g_dyn / np.float32(4096))
-    assert np.all(s3[np.abs(x).reshape(16, -1, 16).max(-1) > 0] == 0x7E)
+    g_small = g_dyn / np.float32(4096)
+    q3, s3, _ = Q.quantize(x, g=g_small)
+    nz = np.abs(x).reshape(16, -1, 16).max(-1) > 0
+    assert np.all(s3[nz] == 0x7E)
+    # ... and the block maxima saturate to the largest value, 6 * 448 * g
+    xh = np.abs(Q.dequantize(q3, s3, g_small)).reshape(16, -1, 16).max(-1)
+    assert np.all(xh[nz] == 6.0 * 448.0 * np.float64(g_small))
     with pytest.raises(ValueError):
         Q.quantize(x, g=np.float32(0))
 
