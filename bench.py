@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill_8192x5120", choices=sorted(W.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--static-scales", action="store_true",
+                   help="MoE: static (calibrated) activation scales, h quantized in the gate_up epilogue")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -114,7 +116,10 @@ def setup_dense(B, name):
           torch.empty(1, dtype=torch.float32, device="cuda"))
     out_dtype = torch.bfloat16 if cfg["out"] == "bf16" else torch.float32
     y = torch.empty((cfg["M"], cfg["N"]), dtype=out_dtype, device="cuda")
-    return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y)
+    # static (calibrated) activation scale: amax of 512 fresh rows / 2688, untimed
+    g_static = B.nvfp4_quantize(W.calibration_rows(name, 512, device="cuda"))[2].clone()
+    xq_static = (torch.empty_like(xq[0]), torch.empty_like(xq[1]), g_static)
+    return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y, xq_static=xq_static)
 
 
 def step_dense(B, st, timer=None):
@@ -165,6 +170,12 @@ def report_dense(st, timer, step_ms):
         iso = st["quantize_iso_ms"]
         extra["quantize_back_to_back"] = dict(avg_ms=iso, gbs=qbytes / (iso * 1e-3) / 1e9,
                                               frac_hbm=qbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    if "quantize_static_ms" in st:
+        sq = st["quantize_static_ms"]
+        extra["quantize_static"] = dict(
+            avg_ms=sq, gbs=qbytes / (sq * 1e-3) / 1e9, frac_hbm=qbytes / (sq * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            note="static global scale calibrated on 512 other rows (amax/2688): one streaming pass; "
+                 "timed in the step, after the GEMM")
     value = flops / (step_ms * 1e-3) / 1e12
     config = dict(workload=st["name"], M=M, N=N, K=K, x=cfg["x_dtype"], out=cfg["out"],
                   weights="NVFP4, quantized offline (static)", activations="NVFP4, dynamic, quantized in the step")
@@ -174,13 +185,46 @@ def report_dense(st, timer, step_ms):
 # ------------------------------------------------------------------- MoE
 
 
-def setup_moe(B, name):
+def setup_moe(B, name, static=False):
     cfg = W.WORKLOADS[name]
     inp = W.moe_inputs(name, device="cuda")
     wgu = B.nvfp4_quantize_batched(inp["w_gate_up"])
     wd = B.nvfp4_quantize_batched(inp["w_down"])
     del inp["w_gate_up"], inp["w_down"]
-    return dict(cfg=cfg, name=name, x=inp["x"], logits=inp["logits"], k=inp["k"], wgu=wgu, wd=wd)
+    st = dict(cfg=cfg, name=name, x=inp["x"], logits=inp["logits"], k=inp["k"], wgu=wgu, wd=wd,
+              static=static)
+    if static:
+        # calibrate the two activation scales (max over a batch of other tokens), untimed
+        T_cal = min(cfg["T"], 2048)
+        lg, xc = W.moe_calibration_inputs(name, T_cal, device="cuda")
+        r = B.nvfp4_moe_route(lg, inp["k"])
+        xq = B.nvfp4_quantize(xc)
+        h = B.nvfp4_moe_grouped_gemm(xq, r["src_row"], r["offsets"], T_cal * inp["k"], wgu,
+                                     epilogue=B.NVFP4_EPI_SILU_GATE, out_dtype=torch.float32)
+        st["gx"] = xq[2].clone()
+        st["gh"] = B.nvfp4_quantize(h)[2].clone()
+        del h
+    return st
+
+
+def step_moe_static(B, st, timer=None):
+    T = st["x"].shape[0]
+    k = st["k"]
+    R = T * k
+    m = [timer.mark()] if timer else None
+    r = B.nvfp4_moe_route(st["logits"], k)
+    if timer: m.append(timer.mark())
+    xq = B.nvfp4_quantize(st["x"], g=st["gx"])
+    if timer: m.append(timer.mark())
+    hq = B.nvfp4_moe_grouped_gemm_silu_nvfp4(xq, r["src_row"], r["offsets"], R, st["wgu"], st["gh"])
+    if timer: m.append(timer.mark())
+    y = B.nvfp4_moe_grouped_gemm(hq, None, r["offsets"], R, st["wd"], out_dtype=torch.float32)
+    if timer: m.append(timer.mark())
+    B.nvfp4_moe_combine(y, r["topk_w"], r["inv"])
+    if timer:
+        m.append(timer.mark())
+        for i, n in enumerate(["route", "quantize_x", "gate_up", "down", "combine"]):
+            timer.add(n, m[i], m[i + 1])
 
 
 def step_moe(B, st, timer=None):
@@ -215,17 +259,22 @@ def report_moe(st, timer, step_ms):
     flops = f_gu + f_d
     gu_ms = timer.mean_ms("gate_up")
     gu_tflops = f_gu / (gu_ms * 1e-3) / 1e12
+    kernel = "nvfp4 gemm_dma_kernel" if H % 256 == 0 else "nvfp4 gemm_kernel"
+    kernel += " (grouped, SiLU gate" + (" -> NVFP4 h)" if st["static"] else ")")
     roof = dict(bound="mfma", achieved=gu_tflops, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel="nvfp4 gemm_dma_kernel (grouped, SiLU gate)" if H % 256 == 0 else "nvfp4 gemm_kernel (grouped, SiLU gate)",
-                traffic=None, per_launch=dict(flops=f_gu, avg_ms=gu_ms))
+                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel=kernel, traffic=None,
+                per_launch=dict(flops=f_gu, avg_ms=gu_ms))
     parts = {n: timer.mean_ms(n) for n in timer.names}
     d_ms = parts["down"]
-    qh_bytes = quant_bytes(R * I, 4)
-    extra = dict(stages_ms=parts, down=dict(tflops=f_d / (d_ms * 1e-3) / 1e12),
-                 quantize_h=dict(gbs=qh_bytes / (parts["quantize_h"] * 1e-3) / 1e9))
+    extra = dict(stages_ms=parts, down=dict(tflops=f_d / (d_ms * 1e-3) / 1e12))
+    if "quantize_h" in parts:
+        qh_bytes = quant_bytes(R * I, 4)
+        extra["quantize_h"] = dict(gbs=qh_bytes / (parts["quantize_h"] * 1e-3) / 1e9)
     value = flops / (step_ms * 1e-3) / 1e12
     config = dict(workload=st["name"], T=T, E=E, k=k, H=H, I=I, x="bf16", out="bf16",
-                  experts="NVFP4 gate_up [2I x H] and down [H x I], quantized offline")
+                  experts="NVFP4 gate_up [2I x H] and down [H x I], quantized offline",
+                  activation_scales="static (calibrated on 2048 other tokens), h quantized in the "
+                                    "gate_up epilogue" if st["static"] else "dynamic")
     return value, "TFLOP/s", roof, extra, config
 
 
@@ -289,8 +338,11 @@ def main():
         st, step, report = setup_dense(B, args.workload), step_dense, report_dense
         names = ["quantize", "gemm"]
     else:
-        st, step, report = setup_moe(B, args.workload), step_moe, report_moe
-        names = ["route", "quantize_x", "gate_up", "quantize_h", "down", "combine"]
+        st, report = setup_moe(B, args.workload, static=args.static_scales), report_moe
+        if args.static_scales:
+            step, names = step_moe_static, ["route", "quantize_x", "gate_up", "down", "combine"]
+        else:
+            step, names = step_moe, ["route", "quantize_x", "gate_up", "quantize_h", "down", "combine"]
 
     for _ in range(args.warmup):
         step(B, st)
@@ -324,6 +376,17 @@ def main():
         q1.record()
         torch.cuda.synchronize()
         st["quantize_iso_ms"] = q0.elapsed_time(q1) / args.steps
+        # the static-scale quantizer where it would sit in a step: after a GEMM
+        sq = []
+        for _ in range(args.steps):
+            B.nvfp4_gemm(st["xq"], st["wq"], out=st["y"])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.nvfp4_quantize(st["x"], g=st["xq_static"][2], out=st["xq_static"])
+            e1.record()
+            sq.append((e0, e1))
+        torch.cuda.synchronize()
+        st["quantize_static_ms"] = sum(a.elapsed_time(b) for a, b in sq) / len(sq)
 
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")

@@ -150,7 +150,7 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
     else:
         q, s, gg = out
     static = g is not None
-    if static:
+    if static and gg.data_ptr() != g.data_ptr():
         gg.copy_(g.reshape(1))
     hs = _stream(stream)
     ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, hs)

@@ -51,6 +51,33 @@ def _normal(shape, std, gen, device):
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
 
 
+def calibration_rows(name, rows, device="cpu"):
+    """Activations of a dense workload's layer for calibrating a static global
+    scale: ``rows`` fresh rows (their own seed) under the workload's fixed
+    per-channel scales, so they follow the same distribution as X."""
+    cfg = WORKLOADS[name]
+    K = cfg["K"]
+    if name == "prefill_8192x5120":
+        # the channel scales c are drawn after Z in the workload's own stream
+        gen = _gen(cfg["seed"], device)
+        _normal((cfg["M"], K), 1.0, gen, device)
+        c = torch.exp(_normal((K,), 1.0, gen, device))
+        z = _normal((rows, K), 1.0, _gen(cfg["seed"] + 1000, device), device)
+        return (z * c[None, :]).to(torch.bfloat16)
+    dtype = torch.float32 if cfg["x_dtype"] == "f32" else torch.bfloat16
+    return _normal((rows, K), 1.0, _gen(cfg["seed"] + 1000, device), device).to(dtype)
+
+
+def moe_calibration_inputs(name, T, device="cpu"):
+    """(logits, X) of ``T`` fresh tokens (their own seed) for an MoE workload:
+    the batch a static activation scale is calibrated on."""
+    cfg = WORKLOADS[name]
+    gen = _gen(cfg["seed"] + 1000, device)
+    logits = _normal((T, cfg["E"]), 1.0, gen, device)
+    x = _normal((T, cfg["H"]), 1.0, gen, device).to(torch.bfloat16)
+    return logits, x
+
+
 def linear_inputs(name, device="cpu", M=None):
     """(X, W) for a dense workload; ``M`` overrides the row count of X."""
     cfg = WORKLOADS[name]
