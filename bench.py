@@ -154,8 +154,10 @@ def report_dense(st, timer, step_ms):
         roof = dict(bound="hbm", achieved=gemm_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=gemm_gbs / HBM_PEAK_GBS)
     traffic = None
-    if st["name"] == "prefill_8192x5120":
-        traffic = profiled_traffic("gemm_prefill_8192x5120x25600.md", "moe_nvfp4_quantize_amd/csrc/gemm.hip")
+    profile = {"prefill_8192x5120": "gemm_prefill_8192x5120x25600.md",
+               "lmhead_128x151936": "gemm_lmhead_128x151936x2048.md"}.get(st["name"])
+    if profile:
+        traffic = profiled_traffic(profile, "moe_nvfp4_quantize_amd/csrc/gemm.hip")
     kernel = "nvfp4 gemm_dma_kernel" if K % 256 == 0 else "nvfp4 gemm_kernel"
     roof.update(kernel=kernel, traffic=traffic,
                 per_launch=dict(flops=flops, algorithmic_bytes=gemm_bytes, avg_ms=gemm_ms))
