@@ -120,6 +120,27 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type,
                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Offline (weight) quantize with four-over-six block scales (Nemotron 3.5
+ * Lightning QAD page, PTQ recipe table: "4/6", the block maximum mapped to
+ * E2M1 magnitude 6 or 4, whichever gives the lower squared error; such
+ * searched scales are then kept frozen).
+ *
+ * Same layout, global scale (g[b] = amax_b/2688 per matrix) and workspace as
+ * nvfp4_quantize_batched; for every block both candidates are encoded:
+ *   M = 6: s6 = E4M3(min(bmax/(6*g), 448)), the plain scale;
+ *   M = 4: s4 = E4M3(min(bmax/(4*g), 448));   (a zero raised to 2^-9)
+ * codes from r = 1/(s*g) as in nvfp4_quantize, and the block keeps M = 4 iff
+ * its float32 error sum E4 < E6, where E = sum over the 16 elements in order of
+ * d*d, d = x - fl(e2m1(code) * s * g) (each operation rounded once); ties keep
+ * the plain block.  Decoding is unchanged: any NVFP4 consumer reads the result.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_4over6(const void *x, nvfp4_dtype x_type,
+                                   int64_t batch, int64_t rows, int64_t cols,
+                                   uint8_t *q, uint8_t *s, float *g,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Dense W4A4 GEMM (Model-Optimizer QAD tutorial for Qwen3.6-35B-A3B, section
  * "Why W4A4 rather than W4A16": both operands NVFP4, wide accumulation).
  *

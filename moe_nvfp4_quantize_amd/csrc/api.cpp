@@ -142,6 +142,24 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type, int64_t b
   return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, (uint32_t)batch, nullptr, stream));
 }
 
+nvfp4_status nvfp4_quantize_4over6(const void *x, nvfp4_dtype x_type, int64_t batch,
+                                   int64_t rows, int64_t cols, uint8_t *q, uint8_t *s, float *g,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_type) || !quant_shape_ok(rows, cols) || batch < 0 || batch > 65535)
+    return NVFP4_ERR_INVALID_ARG;
+  if (batch == 0) return NVFP4_OK;
+  if (!g || (rows > 0 && (!x || !q || !s))) return NVFP4_ERR_INVALID_ARG;
+  const size_t need = quant_ws(batch, rows, cols, false);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3u))
+    return NVFP4_ERR_INVALID_ARG;
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  const bool vec = aligned16(x) && (cols * (int64_t)dtype_size(x_type)) % 16 == 0;
+  QuantParams p = make_quant(x, rows, cols, cols, q, s, g, workspace, 0);
+  p.four6 = 1;
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, (uint32_t)batch, nullptr, stream));
+}
+
 nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g,
                         const uint8_t *b_q, const uint8_t *b_s, const float *b_g, int64_t M,
                         int64_t N, int64_t K, void *c, nvfp4_dtype c_type, int64_t ldc,

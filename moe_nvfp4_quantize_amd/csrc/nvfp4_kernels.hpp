@@ -40,6 +40,7 @@ struct QuantParams {
   float *partials;               // [batch][P] workspace
   uint32_t P;                    // partials per matrix
   int static_global;
+  int four6;  // block scale by the four-over-six rule (two-pass path)
 };
 
 uint32_t quantize_partials_per_matrix(uint64_t units);

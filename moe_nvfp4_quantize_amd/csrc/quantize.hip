@@ -135,6 +135,66 @@ __device__ __forceinline__ void encode_block(const uint32_t w[Raw<T>::W], float 
   __builtin_nontemporal_store((uint8_t)sc, s);
 }
 
+// 16 E2M1 codes of x * r as two dwords (element 2i in the low nibble of byte i)
+template <typename T>
+__device__ __forceinline__ uint64_t encode16(const uint32_t w[Raw<T>::W], float r) {
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 0) * r, elem<T>(w, 1) * r, 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 2) * r, elem<T>(w, 3) * r, 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 4) * r, elem<T>(w, 5) * r, 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, elem<T>(w, 6) * r, elem<T>(w, 7) * r, 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 8) * r, elem<T>(w, 9) * r, 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 10) * r, elem<T>(w, 11) * r, 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 12) * r, elem<T>(w, 13) * r, 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, elem<T>(w, 14) * r, elem<T>(w, 15) * r, 1.0f, 3);
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// Sum of squared errors of a block's 16 decoded values against x, in float32
+// and in element order: d = x - fl(v * g) with v = e2m1(code) * s exact.
+template <typename T>
+__device__ __forceinline__ float block_sse(const uint32_t w[Raw<T>::W], uint64_t codes, float sv,
+                                           float g) {
+  float e = 0.0f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t c = (uint32_t)(codes >> (32 * half));
+    float2v v[4];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xh = (v[i / 2][i % 2] * sv) * g;
+      const float d = elem<T>(w, 8 * half + i) - xh;
+      e = e + d * d;
+    }
+  }
+  return e;
+}
+
+// Four-over-six encode of one block: the block max mapped to E2M1 magnitude 6
+// (plain) or 4, whichever has the lower float32 squared error (ties: 6).
+// Nemotron 3.5 Lightning QAD page, PTQ recipe table ("4/6").
+template <typename T>
+__device__ __forceinline__ void encode_block_4over6(const uint32_t w[Raw<T>::W], float bmax, float g,
+                                                    float six_g, float inv_six_g, float four_g,
+                                                    float inv_four_g, const float *rtab, uint8_t *q,
+                                                    uint8_t *s) {
+  const uint32_t sc6 = block_scale_code(bmax, six_g, inv_six_g);
+  const uint32_t sc4 = block_scale_code(bmax, four_g, inv_four_g);
+  const uint64_t c6 = encode16<T>(w, rtab[sc6]);
+  const uint64_t c4 = encode16<T>(w, rtab[sc4]);
+  const float e6 = block_sse<T>(w, c6, e4m3_value(sc6), g);
+  const float e4 = block_sse<T>(w, c4, e4m3_value(sc4), g);
+  const bool take4 = e4 < e6;
+  __builtin_nontemporal_store(take4 ? c4 : c6, reinterpret_cast<uint64_t *>(q));
+  __builtin_nontemporal_store((uint8_t)(take4 ? sc4 : sc6), s);
+}
+
 // r = 1 / (s * g) for every positive E4M3 code s (index 1..126); one per thread.
 __device__ __forceinline__ void fill_rtab(float *rtab, float g) {
   const uint32_t c = threadIdx.x;
@@ -163,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) 
   if (threadIdx.x == 0) p.partials[(int64_t)b * p.P + blockIdx.x] = m;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool FOUR6 = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ float rtab[128];
   const uint32_t b = blockIdx.y;
@@ -189,7 +249,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     uint32_t w[Raw<T>::W];
     load_raw<T, VEC>(x + (int64_t)row * p.ld + blk * 16, w);
     // u == row * nbpr + blk and q/s rows are dense: offsets are u*8 and u
-    encode_block<T>(w, raw_max<T>(w), six_g, inv_six_g, rtab, q + (int64_t)u * 8, s + u);
+    if (FOUR6)
+      encode_block_4over6<T>(w, raw_max<T>(w), g, six_g, inv_six_g, 4.0f * g, 1.0f / (4.0f * g), rtab,
+                             q + (int64_t)u * 8, s + u);
+    else
+      encode_block<T>(w, raw_max<T>(w), six_g, inv_six_g, rtab, q + (int64_t)u * 8, s + u);
   }
 }
 
@@ -298,7 +362,7 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
   }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool FOUR6 = false>
 hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t stream) {
   uint64_t wg = ((uint64_t)p.units + kThreads - 1) / kThreads;
   if (wg < 1) wg = 1;
@@ -308,7 +372,7 @@ hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  quantize_kernel<T, VEC><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
+  quantize_kernel<T, VEC, FOUR6><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -376,6 +440,13 @@ uint32_t quantize_partials_per_matrix(uint64_t units) {
 
 hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
                            hipStream_t stream) {
+  if (p.four6) {  // offline weights: the two-pass path
+    if (bf16)
+      return vec ? launch_two_pass<uint16_t, true, true>(p, batch, stream)
+                 : launch_two_pass<uint16_t, false, true>(p, batch, stream);
+    return vec ? launch_two_pass<float, true, true>(p, batch, stream)
+               : launch_two_pass<float, false, true>(p, batch, stream);
+  }
   // single-read resident path: dynamic scale, one matrix, fits in registers
   if (!p.static_global && batch == 1 && st != nullptr) {
     const uint32_t cus = resident_capacity_wgs();

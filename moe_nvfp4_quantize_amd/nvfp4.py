@@ -39,6 +39,8 @@ SIGNATURES = {
     "nvfp4_quantize_batched_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quantize_batched": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
                                               _SZ, _P]),
+    "nvfp4_quantize_4over6": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
+                                             _SZ, _P]),
     "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _I64,
                                   _P]),
     "nvfp4_moe_route_workspace_size": (_SZ, [_I64, _I32, _I32]),
@@ -158,6 +160,26 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
                             _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_quantize", st)
     return q, s, gg
+
+
+def nvfp4_quantize_4over6(x, stream=None):
+    """Offline quantize with four-over-six block scales of a 2-D [rows, cols] or batched
+    [B, rows, cols] contiguous GPU tensor -> (q, s, g); one global scale per matrix."""
+    lib = load_library()
+    _on_gpu(x)
+    if not x.is_contiguous() or x.dim() not in (2, 3):
+        raise ValueError("x must be a contiguous 2-D or 3-D tensor")
+    single = x.dim() == 2
+    xb = x.unsqueeze(0) if single else x
+    B, rows, cols = xb.shape
+    q = torch.empty((B, rows, cols // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((B, rows, cols // 16), dtype=torch.uint8, device=x.device)
+    g = torch.empty(B, dtype=torch.float32, device=x.device)
+    ws = _ws(lib.nvfp4_quantize_batched_workspace_size(B, rows, cols), x.device)
+    st = lib.nvfp4_quantize_4over6(_ptr(xb), _dtype_code(x.dtype), B, rows, cols, _ptr(q), _ptr(s),
+                                   _ptr(g), _ptr(ws), ws.numel(), _stream(stream))
+    _check("nvfp4_quantize_4over6", st)
+    return (q[0], s[0], g[:1]) if single else (q, s, g)
 
 
 def nvfp4_quantize_batched(x, stream=None):
