@@ -120,6 +120,25 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type,
                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Quantize-dequantize ("fake quantization"), the simulated-quantization
+ * forward of quantization-aware distillation (QAD page: NVFP4 simulated in
+ * the forward pass, with scales either recomputed every step -- dynamic -- or
+ * calibrated once and frozen -- static_global != 0).
+ *
+ * y[r][c] = fl(e2m1(code) * e4m3(s) * g) for the codes and block scales that
+ * nvfp4_quantize computes from x with the same rows, cols, g and mode; the
+ * product e2m1 * e4m3 is exact, the multiplication by g rounds once to float32
+ * and a bf16 y rounds that once more (nearest even).  y has x's type, row
+ * stride ld_y >= cols (elements); y may be x itself (in place) when
+ * ld_y == ld_x.  g, static_global, workspace: as for nvfp4_quantize (the
+ * dynamic g is written).  No codes or scales are stored.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype x_type, int64_t rows,
+                       int64_t cols, int64_t ld_x, void *y, int64_t ld_y,
+                       float *g, int static_global, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Offline (weight) quantize with four-over-six block scales (Nemotron 3.5
  * Lightning QAD page, PTQ recipe table: "4/6", the block maximum mapped to
  * E2M1 magnitude 6 or 4, whichever gives the lower squared error; such

@@ -142,6 +142,33 @@ nvfp4_status nvfp4_quantize_batched(const void *x, nvfp4_dtype x_type, int64_t b
   return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, (uint32_t)batch, nullptr, stream));
 }
 
+nvfp4_status nvfp4_qdq(const void *x, nvfp4_dtype x_type, int64_t rows, int64_t cols,
+                       int64_t ld_x, void *y, int64_t ld_y, float *g, int static_global,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_type) || !quant_shape_ok(rows, cols) || ld_x < cols || ld_y < cols || !g)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !y)) return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && (ld_x > kI32Max * 64ll || ld_y > kI32Max * 64ll)) return NVFP4_ERR_INVALID_ARG;
+  if (x && y && x == y && ld_x != ld_y) return NVFP4_ERR_INVALID_ARG;
+  if (!static_global) {
+    const size_t need = quant_ws(1, rows, cols, true);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+      return NVFP4_ERR_INVALID_ARG;
+  } else if (rows == 0) {
+    return NVFP4_OK;
+  }
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  const int64_t es = (int64_t)dtype_size(x_type);
+  const bool vec = aligned16(x) && aligned16(y) && (ld_x * es) % 16 == 0 && (ld_y * es) % 16 == 0;
+  ResidentState *rs = static_cast<ResidentState *>(workspace);
+  void *partials = workspace ? static_cast<uint8_t *>(workspace) + kResidentStateBytes : nullptr;
+  QuantParams p = make_quant(x, rows, cols, ld_x, nullptr, nullptr, g, partials, static_global ? 1 : 0);
+  p.y = y;
+  p.ld_y = ld_y;
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, rs, stream));
+}
+
 nvfp4_status nvfp4_quantize_4over6(const void *x, nvfp4_dtype x_type, int64_t batch,
                                    int64_t rows, int64_t cols, uint8_t *q, uint8_t *s, float *g,
                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {

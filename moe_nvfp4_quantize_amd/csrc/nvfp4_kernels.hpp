@@ -41,6 +41,10 @@ struct QuantParams {
   uint32_t P;                    // partials per matrix
   int static_global;
   int four6;  // block scale by the four-over-six rule (two-pass path)
+  // quantize-dequantize: y [rows][ld_y] of the input type receives the decoded
+  // values instead of q/s being written (nullptr: plain quantize)
+  void *y;
+  int64_t ld_y;
 };
 
 uint32_t quantize_partials_per_matrix(uint64_t units);

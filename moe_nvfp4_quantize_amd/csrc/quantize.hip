@@ -195,6 +195,54 @@ __device__ __forceinline__ void encode_block_4over6(const uint32_t w[Raw<T>::W],
   __builtin_nontemporal_store((uint8_t)(take4 ? sc4 : sc6), s);
 }
 
+// Quantize-dequantize of one block: the plain encode, then every value decoded
+// back, fl32(e2m1 * s * g) (e2m1 * s exact), written in T (bf16: rounded to
+// nearest even).  QAD page: the simulated-quantization forward.
+template <typename T, bool VEC>
+__device__ __forceinline__ void qdq_block(const uint32_t w[Raw<T>::W], float bmax, float six_g,
+                                          float inv_six_g, const float *rtab, float g, T *y) {
+  const uint32_t sc = block_scale_code(bmax, six_g, inv_six_g);
+  const uint64_t codes = encode16<T>(w, rtab[sc]);
+  const float sv = e4m3_value(sc);
+  float o[16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t c = (uint32_t)(codes >> (32 * half));
+    float2v v[4];
+    v[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    v[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+    v[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+    v[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[8 * half + i] = (v[i / 2][i % 2] * sv) * g;
+  }
+  if constexpr (sizeof(T) == 2) {
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pk[i] = float_to_bf16_bits(o[2 * i]) | (float_to_bf16_bits(o[2 * i + 1]) << 16);
+    if (VEC) {
+      u32x4 *y4 = reinterpret_cast<u32x4 *>(y);
+      __builtin_nontemporal_store((u32x4){pk[0], pk[1], pk[2], pk[3]}, y4);
+      __builtin_nontemporal_store((u32x4){pk[4], pk[5], pk[6], pk[7]}, y4 + 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = (T)(pk[i / 2] >> (16 * (i % 2)));
+    }
+  } else {
+    if (VEC) {
+      u32x4 *y4 = reinterpret_cast<u32x4 *>(y);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        __builtin_nontemporal_store((u32x4){f2u(o[4 * k]), f2u(o[4 * k + 1]), f2u(o[4 * k + 2]),
+                                            f2u(o[4 * k + 3])}, y4 + k);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = o[i];
+    }
+  }
+}
+
 // r = 1 / (s * g) for every positive E4M3 code s (index 1..126); one per thread.
 __device__ __forceinline__ void fill_rtab(float *rtab, float g) {
   const uint32_t c = threadIdx.x;
@@ -223,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) 
   if (threadIdx.x == 0) p.partials[(int64_t)b * p.P + blockIdx.x] = m;
 }
 
-template <typename T, bool VEC, bool FOUR6 = false>
+template <typename T, bool VEC, bool FOUR6 = false, bool QDQ = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ float rtab[128];
   const uint32_t b = blockIdx.y;
@@ -249,7 +297,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     uint32_t w[Raw<T>::W];
     load_raw<T, VEC>(x + (int64_t)row * p.ld + blk * 16, w);
     // u == row * nbpr + blk and q/s rows are dense: offsets are u*8 and u
-    if (FOUR6)
+    if (QDQ)
+      qdq_block<T, VEC>(w, raw_max<T>(w), six_g, inv_six_g, rtab, g,
+                        static_cast<T *>(p.y) + (int64_t)row * p.ld_y + blk * 16);
+    else if (FOUR6)
       encode_block_4over6<T>(w, raw_max<T>(w), g, six_g, inv_six_g, 4.0f * g, 1.0f / (4.0f * g), rtab,
                              q + (int64_t)u * 8, s + u);
     else
@@ -282,7 +333,7 @@ __device__ float whole_tensor_max(const QuantParams &p) {
 // finish flips the parity.  A wait that runs past its bound (workgroups not
 // co-resident) is not an error: that workgroup reads the whole tensor itself,
 // which yields the same max.
-template <typename T, bool VEC, int U, int NT>
+template <typename T, bool VEC, int U, int NT, bool QDQ = false>
 __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentState *st) {
   __shared__ float rtab[128];
   __shared__ uint32_t s_fallback;
@@ -349,7 +400,15 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const uint32_t u = i * stride + blockIdx.x * NT + tid;
-    if (u < p.units) encode_block<T>(w[i], bmax[i], six_g, inv_six_g, rtab, p.q + (int64_t)u * 8, p.s + u);
+    if (u < p.units) {
+      if (QDQ) {
+        const uint32_t row = p.div_nbpr.div(u);
+        qdq_block<T, VEC>(w[i], bmax[i], six_g, inv_six_g, rtab, g,
+                          static_cast<T *>(p.y) + (int64_t)row * p.ld_y + (u - row * p.nbpr) * 16);
+      } else {
+        encode_block<T>(w[i], bmax[i], six_g, inv_six_g, rtab, p.q + (int64_t)u * 8, p.s + u);
+      }
+    }
   }
 
   // the last workgroup out hands the other slot array to the next launch
@@ -362,7 +421,7 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
   }
 }
 
-template <typename T, bool VEC, bool FOUR6 = false>
+template <typename T, bool VEC, bool FOUR6 = false, bool QDQ = false>
 hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t stream) {
   uint64_t wg = ((uint64_t)p.units + kThreads - 1) / kThreads;
   if (wg < 1) wg = 1;
@@ -372,7 +431,7 @@ hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  quantize_kernel<T, VEC, FOUR6><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
+  quantize_kernel<T, VEC, FOUR6, QDQ><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -390,36 +449,36 @@ uint32_t resident_capacity_wgs() {
   return cached[dev] > 0 ? (uint32_t)cached[dev] : 0u;
 }
 
-template <typename T, bool VEC, int U, int NT>
+template <typename T, bool VEC, int U, int NT, bool QDQ>
 hipError_t launch_resident_u(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
-  resident_kernel<T, VEC, U, NT><<<G, NT, 0, stream>>>(p, st);
+  resident_kernel<T, VEC, U, NT, QDQ><<<G, NT, 0, stream>>>(p, st);
   return hipGetLastError();
 }
 
 // Blocks per thread U and workgroup size NT: 1024 threads (four waves per
 // SIMD, at most 128 VGPRs) while U stays small, 512 threads (256 VGPRs) for
 // the largest tensors.  Returns hipErrorInvalidValue when no variant fits.
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool QDQ>
 hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
   const uint64_t n = p.units;
   auto need = [&](uint64_t nt) { return (n + (uint64_t)G * nt - 1) / ((uint64_t)G * nt); };
   const uint64_t u1024 = need(1024), u512 = need(512);
   if constexpr (sizeof(T) == 2) {
-    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024>(p, st, G, stream);
-    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024>(p, st, G, stream);
-    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024>(p, st, G, stream);
-    if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024>(p, st, G, stream);
-    if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024>(p, st, G, stream);
-    if (u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024>(p, st, G, stream);
-    if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512>(p, st, G, stream);
-    if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512>(p, st, G, stream);
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, QDQ>(p, st, G, stream);
+    if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, QDQ>(p, st, G, stream);
+    if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, QDQ>(p, st, G, stream);
   } else {
-    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024>(p, st, G, stream);
-    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024>(p, st, G, stream);
-    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024>(p, st, G, stream);
-    if (u512 <= 6) return launch_resident_u<T, VEC, 6, 512>(p, st, G, stream);
-    if (u512 <= 8) return launch_resident_u<T, VEC, 8, 512>(p, st, G, stream);
-    if (u512 <= 10) return launch_resident_u<T, VEC, 10, 512>(p, st, G, stream);
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, QDQ>(p, st, G, stream);
+    if (u512 <= 6) return launch_resident_u<T, VEC, 6, 512, QDQ>(p, st, G, stream);
+    if (u512 <= 8) return launch_resident_u<T, VEC, 8, 512, QDQ>(p, st, G, stream);
+    if (u512 <= 10) return launch_resident_u<T, VEC, 10, 512, QDQ>(p, st, G, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -453,12 +512,26 @@ hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, R
     uint32_t G = (uint32_t)std::min<uint64_t>(((uint64_t)p.units + 511) / 512, cus);
     G = std::min<uint32_t>(std::max<uint32_t>(G, 1u), kMaxResidentWGs);
     if (cus > 0 && resident_fits(p.units, G, bf16)) {
+      if (p.y) {
+        if (bf16)
+          return vec ? launch_resident<uint16_t, true, true>(p, st, G, stream)
+                     : launch_resident<uint16_t, false, true>(p, st, G, stream);
+        return vec ? launch_resident<float, true, true>(p, st, G, stream)
+                   : launch_resident<float, false, true>(p, st, G, stream);
+      }
       if (bf16)
-        return vec ? launch_resident<uint16_t, true>(p, st, G, stream)
-                   : launch_resident<uint16_t, false>(p, st, G, stream);
-      return vec ? launch_resident<float, true>(p, st, G, stream)
-                 : launch_resident<float, false>(p, st, G, stream);
+        return vec ? launch_resident<uint16_t, true, false>(p, st, G, stream)
+                   : launch_resident<uint16_t, false, false>(p, st, G, stream);
+      return vec ? launch_resident<float, true, false>(p, st, G, stream)
+                 : launch_resident<float, false, false>(p, st, G, stream);
     }
+  }
+  if (p.y) {
+    if (bf16)
+      return vec ? launch_two_pass<uint16_t, true, false, true>(p, batch, stream)
+                 : launch_two_pass<uint16_t, false, false, true>(p, batch, stream);
+    return vec ? launch_two_pass<float, true, false, true>(p, batch, stream)
+               : launch_two_pass<float, false, false, true>(p, batch, stream);
   }
   if (bf16)
     return vec ? launch_two_pass<uint16_t, true>(p, batch, stream)

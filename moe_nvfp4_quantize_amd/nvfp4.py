@@ -39,6 +39,8 @@ SIGNATURES = {
     "nvfp4_quantize_batched_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quantize_batched": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
                                               _SZ, _P]),
+    "nvfp4_qdq": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, ctypes.c_int, _P,
+                                 _SZ, _P]),
     "nvfp4_quantize_4over6": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
                                              _SZ, _P]),
     "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _I64,
@@ -160,6 +162,30 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
                             _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_quantize", st)
     return q, s, gg
+
+
+def nvfp4_qdq(x, g=None, out=None, stream=None):
+    """Quantize-dequantize a 2-D f32/bf16 GPU tensor -> (y of x's dtype, g).
+
+    ``g=None``: dynamic global scale (written into the returned g); a float32 [1] GPU
+    tensor: frozen global scale.  ``out`` may be x itself (in place)."""
+    lib = load_library()
+    _on_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along the last dim")
+    rows, cols = x.shape
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or y.stride(1) != 1:
+        raise ValueError("out must match x in shape and dtype")
+    static = g is not None
+    gg = g.reshape(1) if static else torch.empty(1, dtype=torch.float32, device=x.device)
+    hs = _stream(stream)
+    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, hs)
+    st = lib.nvfp4_qdq(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
+                       _ptr(y), y.stride(0) if rows else cols, _ptr(gg), int(static), _ptr(ws),
+                       ws.numel(), hs)
+    _check("nvfp4_qdq", st)
+    return y, gg
 
 
 def nvfp4_quantize_4over6(x, stream=None):
