@@ -106,10 +106,27 @@ class Timer:
 # ----------------------------------------------------------------- dense
 
 
+def _time_ms(fn, reps=5):
+    """Mean time of back-to-back calls, events around the whole run."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def setup_dense(B, name):
     cfg = W.WORKLOADS[name]
     x, w = W.linear_inputs(name, device="cuda")
     wq = B.nvfp4_quantize(w)  # offline static weights, untimed
+    # offline weight quantizers, measured beside the step (not part of it)
+    offline = dict(plain_ms=_time_ms(lambda: B.nvfp4_quantize(w)),
+                   four_over_six_ms=_time_ms(lambda: B.nvfp4_quantize_4over6(w)),
+                   elements=w.numel())
     del w
     xq = (torch.empty((cfg["M"], cfg["K"] // 2), dtype=torch.uint8, device="cuda"),
           torch.empty((cfg["M"], cfg["K"] // 16), dtype=torch.uint8, device="cuda"),
@@ -119,7 +136,9 @@ def setup_dense(B, name):
     # static (calibrated) activation scale: amax of 512 fresh rows / 2688, untimed
     g_static = B.nvfp4_quantize(W.calibration_rows(name, 512, device="cuda"))[2].clone()
     xq_static = (torch.empty_like(xq[0]), torch.empty_like(xq[1]), g_static)
-    return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y, xq_static=xq_static)
+    qdq_ms = _time_ms(lambda: B.nvfp4_qdq(x))
+    return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y, xq_static=xq_static, offline=offline,
+                qdq_ms=qdq_ms)
 
 
 def step_dense(B, st, timer=None):
@@ -172,6 +191,22 @@ def report_dense(st, timer, step_ms):
         iso = st["quantize_iso_ms"]
         extra["quantize_back_to_back"] = dict(avg_ms=iso, gbs=qbytes / (iso * 1e-3) / 1e9,
                                               frac_hbm=qbytes / (iso * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    if "offline" in st:
+        o = st["offline"]
+        in_b = 2 if cfg["x_dtype"] == "bf16" else 4
+        wbytes = quant_bytes(o["elements"], in_b)
+        extra["weights_offline"] = dict(
+            plain_ms=o["plain_ms"], plain_gbs=wbytes / (o["plain_ms"] * 1e-3) / 1e9,
+            four_over_six_ms=o["four_over_six_ms"],
+            four_over_six_gbs=wbytes / (o["four_over_six_ms"] * 1e-3) / 1e9,
+            note="one-time weight quantize (two passes over W: amax, encode); "
+                 "algorithmic bytes count W once")
+    if "qdq_ms" in st:
+        in_b = 2 if cfg["x_dtype"] == "bf16" else 4
+        qb = 2.0 * in_b * M * K
+        extra["qdq"] = dict(avg_ms=st["qdq_ms"], gbs=qb / (st["qdq_ms"] * 1e-3) / 1e9,
+                            frac_hbm=qb / (st["qdq_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            note="dynamic quantize-dequantize of X, back to back; bytes: read + write X")
     if "quantize_static_ms" in st:
         sq = st["quantize_static_ms"]
         extra["quantize_static"] = dict(

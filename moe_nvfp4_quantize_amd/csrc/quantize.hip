@@ -469,7 +469,8 @@ hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, 
     if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, QDQ>(p, st, G, stream);
     if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024, QDQ>(p, st, G, stream);
     if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, QDQ>(p, st, G, stream);
+    // the decode-and-store of quantize-dequantize needs more than 128 VGPRs at 10
+    if (!QDQ && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, QDQ>(p, st, G, stream);
     if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, QDQ>(p, st, G, stream);
     if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, QDQ>(p, st, G, stream);
   } else {
