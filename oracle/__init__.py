@@ -36,6 +36,9 @@ Modules:
     nvfp4    -- two-level quantize and dequantize
     gemm     -- the W4A4 GEMM as an fp64 product of dequantized operands
     moe      -- router top-k + softmax, permutation, expert MLP, combine
+    four_over_six -- weight block scales chosen between maps to 6 and to 4
+    qdq      -- quantize then dequantize (fake quantization)
+    fp8      -- FP8 E4M3 per-tensor W8A8 quantize, dequantize and GEMM
 """
 
 from . import formats, nvfp4, gemm, moe  # noqa: F401
