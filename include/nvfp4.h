@@ -180,6 +180,48 @@ nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g
                         nvfp4_dtype c_type, int64_t ldc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * FP8 W8A8 quantize (QAD tutorial for Qwen3.6-35B-A3B, table of quantized
+ * tensors: the attention projections of the W4A4 checkpoint stay FP8 W8A8;
+ * format-selection guide, section 1: FP8 is W8A8 with per-tensor scaling;
+ * two-level scaling page: the family's FP8 is E4M3 with one FP32 scale per
+ * tensor that the reader multiplies back in).
+ *
+ * x       float32 or bfloat16 [rows][ld_x], ld_x >= cols (elements).
+ * q       [rows][cols] E4M3FN codes, one byte per element, 16-byte aligned.
+ * g       1 float, decode scale: x_hat = e4m3(q) * g.
+ *   static_scale == 0: g := amax/448 (1 if all zero), written by the kernel;
+ *   static_scale != 0: *g is read as given (finite, >= 2^-100).
+ * Encode, float32, round to nearest even: r = 1/g; y = x*r;
+ *   q = sign(x) | E4M3(min(|y|, 448))   (saturates; never the NaN code).
+ * cols > 0, cols % 16 == 0, rows >= 0, rows * cols / 16 < 2^31.
+ * workspace: as for nvfp4_quantize (nvfp4_fp8_quantize_workspace_size bytes,
+ * 256-byte aligned, zero-filled before its first use, then reused; not needed
+ * with static_scale).  The two quantizers may share one workspace.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_fp8_quantize_workspace_size(int64_t rows, int64_t cols);
+nvfp4_status nvfp4_fp8_quantize(const void *x, nvfp4_dtype x_type,
+                                int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t *q, float *g, int static_scale,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 W8A8 GEMM (same passages as nvfp4_fp8_quantize).
+ *
+ *   C[m][n] = a_g * b_g * sum_k e4m3(A[m][k]) * e4m3(B[n][k])
+ * A [M x K] activations and B [N x K] weights (one row per output feature),
+ * dense row-major E4M3FN bytes, 16-byte aligned.  Products are exact,
+ * accumulation is float32, the scales are applied once in the epilogue, the
+ * result is rounded to c_type.  M, N >= 0; K > 0, K % 16 == 0; c is
+ * [M][ldc] of c_type, ldc >= N.  a_g, b_g: device floats.
+ * The fast path needs K % 128 == 0; other K take a general path.
+ * ---------------------------------------------------------------------- */
+nvfp4_status nvfp4_fp8_gemm(const uint8_t *a_q, const float *a_g,
+                            const uint8_t *b_q, const float *b_g,
+                            int64_t M, int64_t N, int64_t K, void *c,
+                            nvfp4_dtype c_type, int64_t ldc, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * MoE routing (two-level scaling page, section "Why only routed experts":
  * each token uses k of E routed experts chosen by a BF16 router).
  *

@@ -24,7 +24,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "moe.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "fp8_gemm.hip", "moe.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -206,6 +206,51 @@ nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g
   return from_hip(launch_gemm(p, c_type == NVFP4_BF16 ? OutType::BF16 : OutType::F32, stream));
 }
 
+size_t nvfp4_fp8_quantize_workspace_size(int64_t rows, int64_t cols) { return quant_ws(1, rows, cols, true); }
+
+nvfp4_status nvfp4_fp8_quantize(const void *x, nvfp4_dtype x_type, int64_t rows, int64_t cols,
+                                int64_t ld_x, uint8_t *q, float *g, int static_scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_type) || !quant_shape_ok(rows, cols) || ld_x < cols || !g)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !q || !aligned16(q))) return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && ld_x > kI32Max * 64ll) return NVFP4_ERR_INVALID_ARG;
+  if (!static_scale) {
+    const size_t need = quant_ws(1, rows, cols, true);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+      return NVFP4_ERR_INVALID_ARG;
+  } else if (rows == 0) {
+    return NVFP4_OK;
+  }
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  const bool vec = aligned16(x) && (ld_x * (int64_t)dtype_size(x_type)) % 16 == 0;
+  ResidentState *rs = static_cast<ResidentState *>(workspace);
+  void *partials = workspace ? static_cast<uint8_t *>(workspace) + kResidentStateBytes : nullptr;
+  QuantParams p = make_quant(x, rows, cols, ld_x, q, nullptr, g, partials, static_scale ? 1 : 0);
+  p.fp8 = 1;
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, rs, stream));
+}
+
+nvfp4_status nvfp4_fp8_gemm(const uint8_t *a_q, const float *a_g, const uint8_t *b_q,
+                            const float *b_g, int64_t M, int64_t N, int64_t K, void *c,
+                            nvfp4_dtype c_type, int64_t ldc, hipStream_t stream) {
+  if (!valid_dtype(c_type) || M < 0 || N < 0 || K <= 0 || K % 16 != 0 || ldc < N)
+    return NVFP4_ERR_INVALID_ARG;
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return NVFP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_q || !a_g || !b_q || !b_g || !c || !aligned16(a_q) || !aligned16(b_q))
+    return NVFP4_ERR_INVALID_ARG;
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  Fp8GemmParams p{};
+  p.a_q = a_q; p.a_g = a_g;
+  p.b_q = b_q; p.b_g = b_g;
+  p.M = (uint32_t)M; p.N = (uint32_t)N; p.K = (uint32_t)K;
+  p.c = c; p.ldc = ldc;
+  return from_hip(launch_fp8_gemm(p, c_type == NVFP4_BF16 ? OutType::BF16 : OutType::F32, stream));
+}
+
 size_t nvfp4_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
   if (T < 0 || E <= 0) return 0;
   return round_up(route_workspace_bytes(T, E, k), 256);

@@ -43,4 +43,45 @@ __device__ __forceinline__ float block_max(float v) {
   return wave_max(r);
 }
 
+// ------------------------------------------------------------ GEMM helpers
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// s_waitcnt with only vmcnt limited (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// s_waitcnt lgkmcnt(0) only
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Swizzle of the four 16-byte pieces of a 64-byte LDS row: piece c of row r
+// is stored at c ^ swz(r).  A 16-byte read of 64 lanes is served 16 lanes
+// (256 bytes, all 64 banks) at a time; in the fragment reads lane l reads
+// piece c of row r0 + l % 32, so 16 consecutive rows must cover the 16
+// distinct 16-byte slots of a 256-byte window: rows r % 4 give the 64-byte
+// quarter, swz(r) = (r / 4) % 4 the piece inside it (measured on gfx950:
+// no bank conflicts, where an unswizzled layout shows 3 of 4 LDS cycles lost).
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 2) & 3u; }
+
+// Which output tile dense workgroup w computes.  Workgroup w runs on XCD
+// w % 8, so each XCD is given a contiguous range of tiles, swept 8 tile-rows
+// at a time so that concurrently running workgroups share A and B tiles in
+// that XCD's L2.
+__device__ __forceinline__ void dense_tile(uint32_t w, uint32_t tiles_m, uint32_t tiles_n,
+                                           uint32_t *tm, uint32_t *tn) {
+  const uint32_t G = tiles_m * tiles_n;
+  const uint32_t q = G / 8, r = G % 8, x = w % 8, local = w / 8;
+  const uint32_t idx = x * q + min(x, r) + local;
+  constexpr uint32_t GM = 8;
+  const uint32_t group = idx / (GM * tiles_n);
+  const uint32_t first_m = group * GM;
+  const uint32_t gsize = min(tiles_m - first_m, GM);
+  const uint32_t pid = idx - group * GM * tiles_n;
+  *tm = first_m + pid % gsize;
+  *tn = pid / gsize;
+}
+
 }  // namespace nvfp4

@@ -45,6 +45,9 @@ struct QuantParams {
   // values instead of q/s being written (nullptr: plain quantize)
   void *y;
   int64_t ld_y;
+  // FP8 W8A8: q [rows][cols] receives one E4M3 code per element, the scale is
+  // amax / 448, s is not written
+  int fp8;
 };
 
 uint32_t quantize_partials_per_matrix(uint64_t units);
@@ -80,6 +83,23 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream);
 bool grouped_nvfp4_out_supported(const GemmParams &p);
 hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epilogue epi,
                                hipStream_t stream);
+
+// --------------------------------------------------------------- FP8 GEMM
+// C [M][N] (ldc) = (a_g b_g) * A B^T with A [M][K] and B [N][K] dense
+// row-major E4M3FN bytes (row stride K), K % 16 == 0, 16-byte aligned bases.
+struct Fp8GemmParams {
+  const uint8_t *a_q;
+  const float *a_g;
+  const uint8_t *b_q;
+  const float *b_g;
+  uint32_t M, N, K;
+  void *c;
+  int64_t ldc;
+};
+
+// whether the direct-to-LDS kernel runs these operands (else the plain one)
+bool fp8_gemm_dma_ok(const Fp8GemmParams &p);
+hipError_t launch_fp8_gemm(const Fp8GemmParams &p, OutType out, hipStream_t stream);
 
 // --------------------------------------------------------------------- MoE
 size_t route_workspace_bytes(int64_t T, int32_t E, int32_t k);

@@ -45,6 +45,14 @@ namespace {
 constexpr int kThreads = 256;          // two-pass kernels
 constexpr uint32_t kSpinLimit = 1u << 15;  // arrival wait bound (tens of milliseconds)
 
+// What a launch writes for each 16-element unit of x.
+enum Mode : int {
+  kNvfp4 = 0,  // packed E2M1 codes + E4M3 block scale
+  kFour6 = 1,  // the same, block scale by the four-over-six rule
+  kQdq = 2,    // the decoded values, in the input type (quantize-dequantize)
+  kFp8 = 3,    // 16 E4M3 codes, one per element, per-tensor scale only
+};
+
 // 16 consecutive elements starting at p, as raw words (bf16: 8 dwords holding
 // two values each; fp32: 16 dwords).  VEC: p is 16-byte aligned.
 template <typename T>
@@ -243,14 +251,40 @@ __device__ __forceinline__ void qdq_block(const uint32_t w[Raw<T>::W], float bma
   }
 }
 
+// FP8 W8A8 (per-tensor E4M3) encode of one 16-element unit: y = x * r with
+// r = 1 / g, clamped to [-448, 448] (a static scale below the data's range
+// saturates instead of producing the NaN code), then the hardware
+// float32 -> E4M3FN convert, two values per instruction, round to nearest
+// even, sign kept on zero.  QAD tutorial, table of quantized tensors (the
+// attention projections stay FP8 W8A8); format-selection guide, section 1
+// (FP8 W8A8 with per-tensor scaling).
+template <typename T>
+__device__ __forceinline__ void encode_unit_fp8(const uint32_t w[Raw<T>::W], float r, uint8_t *q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = __builtin_amdgcn_fmed3f(elem<T>(w, 4 * k + e) * r, -448.0f, 448.0f);
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
+    o[k] = (uint32_t)v;
+  }
+  __builtin_nontemporal_store((u32x4){o[0], o[1], o[2], o[3]}, reinterpret_cast<u32x4 *>(q));
+}
+
 // r = 1 / (s * g) for every positive E4M3 code s (index 1..126); one per thread.
 __device__ __forceinline__ void fill_rtab(float *rtab, float g) {
   const uint32_t c = threadIdx.x;
   if (c < 128) rtab[c] = (c >= 1u && c <= 126u) ? 1.0f / (e4m3_value(c) * g) : 0.0f;
 }
 
+// Per-tensor decode scale from the tensor's max |x|: amax / (6 * 448) for
+// NVFP4 (the block holding amax gets block scale 448), amax / 448 for FP8 (the
+// largest element gets the largest code); 1 for an all-zero tensor.
+template <int MODE>
 __device__ __forceinline__ float global_from_amax(float amax) {
-  return amax > 0.0f ? amax / kGlobalDivisor : 1.0f;
+  return amax > 0.0f ? amax / (MODE == kFp8 ? kE4M3Max : kGlobalDivisor) : 1.0f;
 }
 
 // ------------------------------------------------------------ two-pass path
@@ -271,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) 
   if (threadIdx.x == 0) p.partials[(int64_t)b * p.P + blockIdx.x] = m;
 }
 
-template <typename T, bool VEC, bool FOUR6 = false, bool QDQ = false>
+template <typename T, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
   __shared__ float rtab[128];
   const uint32_t b = blockIdx.y;
@@ -282,12 +316,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     float m = 0.0f;
     for (uint32_t i = threadIdx.x; i < p.P; i += kThreads) m = fmaxf(m, p.partials[(int64_t)b * p.P + i]);
     m = block_max(m);
-    g = global_from_amax(m);
+    g = global_from_amax<MODE>(m);
     if (blockIdx.x == 0 && threadIdx.x == 0) p.g[b] = g;
   }
-  fill_rtab(rtab, g);
+  if (MODE != kFp8) fill_rtab(rtab, g);
   __syncthreads();
-  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g;
+  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g, r8 = 1.0f / g;
   const T *x = static_cast<const T *>(p.x) + (int64_t)b * p.x_mstride;
   uint8_t *q = p.q + (int64_t)b * p.q_mstride;
   uint8_t *s = p.s + (int64_t)b * p.s_mstride;
@@ -297,10 +331,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantParams p) {
     uint32_t w[Raw<T>::W];
     load_raw<T, VEC>(x + (int64_t)row * p.ld + blk * 16, w);
     // u == row * nbpr + blk and q/s rows are dense: offsets are u*8 and u
-    if (QDQ)
+    // (FP8: u*16)
+    if (MODE == kFp8)
+      encode_unit_fp8<T>(w, r8, q + (int64_t)u * 16);
+    else if (MODE == kQdq)
       qdq_block<T, VEC>(w, raw_max<T>(w), six_g, inv_six_g, rtab, g,
                         static_cast<T *>(p.y) + (int64_t)row * p.ld_y + blk * 16);
-    else if (FOUR6)
+    else if (MODE == kFour6)
       encode_block_4over6<T>(w, raw_max<T>(w), g, six_g, inv_six_g, 4.0f * g, 1.0f / (4.0f * g), rtab,
                              q + (int64_t)u * 8, s + u);
     else
@@ -333,7 +370,7 @@ __device__ float whole_tensor_max(const QuantParams &p) {
 // finish flips the parity.  A wait that runs past its bound (workgroups not
 // co-resident) is not an error: that workgroup reads the whole tensor itself,
 // which yields the same max.
-template <typename T, bool VEC, int U, int NT, bool QDQ = false>
+template <typename T, bool VEC, int U, int NT, int MODE>
 __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentState *st) {
   __shared__ float rtab[128];
   __shared__ uint32_t s_fallback;
@@ -390,18 +427,20 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
     a = whole_tensor_max<T, VEC>(p);
     if (tid == 0) __hip_atomic_fetch_add(&st->fallbacks, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const float g = global_from_amax(a);
+  const float g = global_from_amax<MODE>(a);
   if (blockIdx.x == 0 && tid == 0) p.g[0] = g;
-  fill_rtab(rtab, g);
+  if (MODE != kFp8) fill_rtab(rtab, g);
   __syncthreads();
-  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g;
+  const float six_g = 6.0f * g, inv_six_g = 1.0f / six_g, r8 = 1.0f / g;
 
   // phase 2: encode from registers
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const uint32_t u = i * stride + blockIdx.x * NT + tid;
     if (u < p.units) {
-      if (QDQ) {
+      if (MODE == kFp8) {
+        encode_unit_fp8<T>(w[i], r8, p.q + (int64_t)u * 16);
+      } else if (MODE == kQdq) {
         const uint32_t row = p.div_nbpr.div(u);
         qdq_block<T, VEC>(w[i], bmax[i], six_g, inv_six_g, rtab, g,
                           static_cast<T *>(p.y) + (int64_t)row * p.ld_y + (u - row * p.nbpr) * 16);
@@ -421,7 +460,7 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
   }
 }
 
-template <typename T, bool VEC, bool FOUR6 = false, bool QDQ = false>
+template <typename T, bool VEC, int MODE>
 hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t stream) {
   uint64_t wg = ((uint64_t)p.units + kThreads - 1) / kThreads;
   if (wg < 1) wg = 1;
@@ -431,7 +470,7 @@ hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  quantize_kernel<T, VEC, FOUR6, QDQ><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
+  quantize_kernel<T, VEC, MODE><<<dim3(qgrid, batch), kThreads, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -449,37 +488,37 @@ uint32_t resident_capacity_wgs() {
   return cached[dev] > 0 ? (uint32_t)cached[dev] : 0u;
 }
 
-template <typename T, bool VEC, int U, int NT, bool QDQ>
+template <typename T, bool VEC, int U, int NT, int MODE>
 hipError_t launch_resident_u(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
-  resident_kernel<T, VEC, U, NT, QDQ><<<G, NT, 0, stream>>>(p, st);
+  resident_kernel<T, VEC, U, NT, MODE><<<G, NT, 0, stream>>>(p, st);
   return hipGetLastError();
 }
 
 // Blocks per thread U and workgroup size NT: 1024 threads (four waves per
 // SIMD, at most 128 VGPRs) while U stays small, 512 threads (256 VGPRs) for
 // the largest tensors.  Returns hipErrorInvalidValue when no variant fits.
-template <typename T, bool VEC, bool QDQ>
+template <typename T, bool VEC, int MODE>
 hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
   const uint64_t n = p.units;
   auto need = [&](uint64_t nt) { return (n + (uint64_t)G * nt - 1) / ((uint64_t)G * nt); };
   const uint64_t u1024 = need(1024), u512 = need(512);
   if constexpr (sizeof(T) == 2) {
-    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, QDQ>(p, st, G, stream);
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, MODE>(p, st, G, stream);
     // the decode-and-store of quantize-dequantize needs more than 128 VGPRs at 10
-    if (!QDQ && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, QDQ>(p, st, G, stream);
-    if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, QDQ>(p, st, G, stream);
-    if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, QDQ>(p, st, G, stream);
+    if (MODE != kQdq && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, MODE>(p, st, G, stream);
+    if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, MODE>(p, st, G, stream);
+    if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, MODE>(p, st, G, stream);
   } else {
-    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, QDQ>(p, st, G, stream);
-    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, QDQ>(p, st, G, stream);
-    if (u512 <= 6) return launch_resident_u<T, VEC, 6, 512, QDQ>(p, st, G, stream);
-    if (u512 <= 8) return launch_resident_u<T, VEC, 8, 512, QDQ>(p, st, G, stream);
-    if (u512 <= 10) return launch_resident_u<T, VEC, 10, 512, QDQ>(p, st, G, stream);
+    if (u1024 <= 1) return launch_resident_u<T, VEC, 1, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 2) return launch_resident_u<T, VEC, 2, 1024, MODE>(p, st, G, stream);
+    if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, MODE>(p, st, G, stream);
+    if (u512 <= 6) return launch_resident_u<T, VEC, 6, 512, MODE>(p, st, G, stream);
+    if (u512 <= 8) return launch_resident_u<T, VEC, 8, 512, MODE>(p, st, G, stream);
+    if (u512 <= 10) return launch_resident_u<T, VEC, 10, 512, MODE>(p, st, G, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -498,47 +537,48 @@ uint32_t quantize_partials_per_matrix(uint64_t units) {
   return (uint32_t)(wg < kMaxPartials ? wg : kMaxPartials);
 }
 
-hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
-                           hipStream_t stream) {
-  if (p.four6) {  // offline weights: the two-pass path
-    if (bf16)
-      return vec ? launch_two_pass<uint16_t, true, true>(p, batch, stream)
-                 : launch_two_pass<uint16_t, false, true>(p, batch, stream);
-    return vec ? launch_two_pass<float, true, true>(p, batch, stream)
-               : launch_two_pass<float, false, true>(p, batch, stream);
-  }
+namespace {
+
+template <int MODE>
+hipError_t dispatch_two_pass(const QuantParams &p, bool bf16, bool vec, uint32_t batch, hipStream_t stream) {
+  if (bf16)
+    return vec ? launch_two_pass<uint16_t, true, MODE>(p, batch, stream)
+               : launch_two_pass<uint16_t, false, MODE>(p, batch, stream);
+  return vec ? launch_two_pass<float, true, MODE>(p, batch, stream)
+             : launch_two_pass<float, false, MODE>(p, batch, stream);
+}
+
+template <int MODE>
+hipError_t dispatch_resident(const QuantParams &p, bool bf16, bool vec, ResidentState *st, uint32_t G,
+                             hipStream_t stream) {
+  if (bf16)
+    return vec ? launch_resident<uint16_t, true, MODE>(p, st, G, stream)
+               : launch_resident<uint16_t, false, MODE>(p, st, G, stream);
+  return vec ? launch_resident<float, true, MODE>(p, st, G, stream)
+             : launch_resident<float, false, MODE>(p, st, G, stream);
+}
+
+template <int MODE>
+hipError_t dispatch(const QuantParams &p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
+                    hipStream_t stream) {
   // single-read resident path: dynamic scale, one matrix, fits in registers
-  if (!p.static_global && batch == 1 && st != nullptr) {
+  if (MODE != kFour6 && !p.static_global && batch == 1 && st != nullptr) {
     const uint32_t cus = resident_capacity_wgs();
     uint32_t G = (uint32_t)std::min<uint64_t>(((uint64_t)p.units + 511) / 512, cus);
     G = std::min<uint32_t>(std::max<uint32_t>(G, 1u), kMaxResidentWGs);
-    if (cus > 0 && resident_fits(p.units, G, bf16)) {
-      if (p.y) {
-        if (bf16)
-          return vec ? launch_resident<uint16_t, true, true>(p, st, G, stream)
-                     : launch_resident<uint16_t, false, true>(p, st, G, stream);
-        return vec ? launch_resident<float, true, true>(p, st, G, stream)
-                   : launch_resident<float, false, true>(p, st, G, stream);
-      }
-      if (bf16)
-        return vec ? launch_resident<uint16_t, true, false>(p, st, G, stream)
-                   : launch_resident<uint16_t, false, false>(p, st, G, stream);
-      return vec ? launch_resident<float, true, false>(p, st, G, stream)
-                 : launch_resident<float, false, false>(p, st, G, stream);
-    }
+    if (cus > 0 && resident_fits(p.units, G, bf16)) return dispatch_resident<MODE>(p, bf16, vec, st, G, stream);
   }
-  if (p.y) {
-    if (bf16)
-      return vec ? launch_two_pass<uint16_t, true, false, true>(p, batch, stream)
-                 : launch_two_pass<uint16_t, false, false, true>(p, batch, stream);
-    return vec ? launch_two_pass<float, true, false, true>(p, batch, stream)
-               : launch_two_pass<float, false, false, true>(p, batch, stream);
-  }
-  if (bf16)
-    return vec ? launch_two_pass<uint16_t, true>(p, batch, stream)
-               : launch_two_pass<uint16_t, false>(p, batch, stream);
-  return vec ? launch_two_pass<float, true>(p, batch, stream)
-             : launch_two_pass<float, false>(p, batch, stream);
+  return dispatch_two_pass<MODE>(p, bf16, vec, batch, stream);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(QuantParams p, bool bf16, bool vec, uint32_t batch, ResidentState *st,
+                           hipStream_t stream) {
+  if (p.fp8) return dispatch<kFp8>(p, bf16, vec, batch, st, stream);
+  if (p.four6) return dispatch<kFour6>(p, bf16, vec, batch, st, stream);  // offline weights: two-pass
+  if (p.y) return dispatch<kQdq>(p, bf16, vec, batch, st, stream);
+  return dispatch<kNvfp4>(p, bf16, vec, batch, st, stream);
 }
 
 }  // namespace nvfp4

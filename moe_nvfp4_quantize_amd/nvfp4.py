@@ -45,6 +45,10 @@ SIGNATURES = {
                                              _SZ, _P]),
     "nvfp4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _I64,
                                   _P]),
+    "nvfp4_fp8_quantize_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_fp8_quantize": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, ctypes.c_int, _P,
+                                          _SZ, _P]),
+    "nvfp4_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
     "nvfp4_moe_route_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "nvfp4_moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_moe_grouped_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _I32, _I64, _P, _P, _P,
@@ -247,6 +251,55 @@ def nvfp4_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
                         _ptr(out), _dtype_code(out.dtype), out.stride(0) if M else N,
                         _stream(stream))
     _check("nvfp4_gemm", st)
+    return out
+
+
+# ----------------------------------------------------------------------- FP8
+
+
+def nvfp4_fp8_quantize(x, g=None, out=None, stream=None):
+    """FP8 W8A8 quantize of a 2-D f32/bf16 GPU tensor -> (q uint8 [rows, cols], g float32 [1]).
+
+    ``g=None``: dynamic per-tensor scale (amax/448), written into the returned g;
+    a float32 [1] GPU tensor: static scale, used as is.  ``out``: optional (q, g)."""
+    lib = load_library()
+    _on_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along the last dim")
+    rows, cols = x.shape
+    if out is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        gg = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, gg = out
+    static = g is not None
+    if static and gg.data_ptr() != g.data_ptr():
+        gg.copy_(g.reshape(1))
+    hs = _stream(stream)
+    ws = _quantize_ws(lib.nvfp4_fp8_quantize_workspace_size(rows, cols), x.device, hs)
+    st = lib.nvfp4_fp8_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
+                                _ptr(q), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
+    _check("nvfp4_fp8_quantize", st)
+    return q, gg
+
+
+def nvfp4_fp8_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """C = A_hat @ B_hat^T for FP8 tensors a = (q, g) [M, K], b = (q, g) [N, K]."""
+    lib = load_library()
+    a_q, a_g = a
+    b_q, b_g = b
+    _on_gpu(a_q, a_g, b_q, b_g)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError("K mismatch between A and B")
+    if not (a_q.is_contiguous() and b_q.is_contiguous()):
+        raise ValueError("q must be contiguous")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    st = lib.nvfp4_fp8_gemm(_ptr(a_q), _ptr(a_g), _ptr(b_q), _ptr(b_g), M, N, K, _ptr(out),
+                            _dtype_code(out.dtype), out.stride(0) if M else N, _stream(stream))
+    _check("nvfp4_fp8_gemm", st)
     return out
 
 

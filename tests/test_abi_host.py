@@ -163,6 +163,35 @@ def test_combine_rejects(lib):
         assert call(**bad) == INVALID, bad
 
 
+def test_fp8_quantize_rejects(lib):
+    f = lib.nvfp4_fp8_quantize
+    assert lib.nvfp4_fp8_quantize_workspace_size(8192, 5120) == lib.nvfp4_quantize_workspace_size(8192, 5120)
+    ok = dict(x=FAKE, t=B.NVFP4_BF16, rows=4, cols=32, ld=32, q=FAKE, g=FAKE, static=0, ws=FAKE, wsb=4096)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["t"], a["rows"], a["cols"], a["ld"], a["q"], a["g"], a["static"], a["ws"],
+                 a["wsb"], None)
+    for bad in [dict(cols=24), dict(cols=0), dict(rows=-1), dict(ld=16), dict(t=7), dict(x=None),
+                dict(q=None), dict(q=ctypes.c_void_p(0x1008)), dict(g=None), dict(ws=None), dict(wsb=8),
+                dict(ws=ctypes.c_void_p(0x1080)), dict(rows=2 ** 31, cols=16)]:
+        assert call(**bad) == INVALID, bad
+    assert call(rows=0, x=None, q=None, static=1, ws=None, wsb=0) == B.NVFP4_OK
+
+
+def test_fp8_gemm_rejects(lib):
+    f = lib.nvfp4_fp8_gemm
+    ok = dict(aq=FAKE, ag=FAKE, bq=FAKE, bg=FAKE, M=4, N=8, K=64, c=FAKE, t=B.NVFP4_F32, ldc=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["aq"], a["ag"], a["bq"], a["bg"], a["M"], a["N"], a["K"], a["c"], a["t"], a["ldc"], None)
+    for bad in [dict(K=24), dict(K=0), dict(M=-1), dict(ldc=4), dict(t=5), dict(aq=None), dict(bg=None),
+                dict(c=None), dict(N=2 ** 31), dict(bq=ctypes.c_void_p(0x1004))]:
+        assert call(**bad) == INVALID, bad
+    assert call(M=0, aq=None, c=None) == B.NVFP4_OK
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_valid_request_without_device_reports_hip_error(lib):
     # arguments pass validation; the device check then fails on a machine with no GPU
