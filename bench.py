@@ -38,6 +38,7 @@ from moe_nvfp4_quantize_amd import workloads as W  # noqa: E402
 METRIC = "NVFP4 GEMM eff. TFLOPS & quantize GB/s, % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA, TFLOP/s
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense FP4, context only
 
 
@@ -127,6 +128,8 @@ def setup_dense(B, name):
     offline = dict(plain_ms=_time_ms(lambda: B.nvfp4_quantize(w)),
                    four_over_six_ms=_time_ms(lambda: B.nvfp4_quantize_4over6(w)),
                    elements=w.numel())
+    # the same layer in FP8 W8A8 (per-tensor E4M3), weights quantized offline
+    w8 = B.nvfp4_fp8_quantize(w)
     del w
     xq = (torch.empty((cfg["M"], cfg["K"] // 2), dtype=torch.uint8, device="cuda"),
           torch.empty((cfg["M"], cfg["K"] // 16), dtype=torch.uint8, device="cuda"),
@@ -138,7 +141,22 @@ def setup_dense(B, name):
     xq_static = (torch.empty_like(xq[0]), torch.empty_like(xq[1]), g_static)
     qdq_ms = _time_ms(lambda: B.nvfp4_qdq(x))
     return dict(cfg=cfg, name=name, x=x, wq=wq, xq=xq, y=y, xq_static=xq_static, offline=offline,
-                qdq_ms=qdq_ms)
+                qdq_ms=qdq_ms, w8=w8)
+
+
+def measure_fp8(B, st, reps):
+    """FP8 W8A8 layer at the same shape: dynamic per-tensor quantize of X, then
+    the FP8 GEMM, each timed back to back, and the two as a step."""
+    cfg = st["cfg"]
+    x8 = (torch.empty((cfg["M"], cfg["K"]), dtype=torch.uint8, device="cuda"),
+          torch.empty(1, dtype=torch.float32, device="cuda"))
+    q_ms = _time_ms(lambda: B.nvfp4_fp8_quantize(st["x"], out=x8), reps)
+    g_ms = _time_ms(lambda: B.nvfp4_fp8_gemm(x8, st["w8"], out=st["y"]), reps)
+
+    def both():
+        B.nvfp4_fp8_quantize(st["x"], out=x8)
+        B.nvfp4_fp8_gemm(x8, st["w8"], out=st["y"])
+    st["fp8"] = dict(quantize_ms=q_ms, gemm_ms=g_ms, step_ms=_time_ms(both, reps))
 
 
 def step_dense(B, st, timer=None):
@@ -213,6 +231,19 @@ def report_dense(st, timer, step_ms):
             avg_ms=sq, gbs=qbytes / (sq * 1e-3) / 1e9, frac_hbm=qbytes / (sq * 1e-3) / 1e9 / HBM_PEAK_GBS,
             note="static global scale calibrated on 512 other rows (amax/2688): one streaming pass; "
                  "timed in the step, after the GEMM")
+    if "fp8" in st:
+        f = st["fp8"]
+        in_b = 2 if cfg["x_dtype"] == "bf16" else 4
+        f8_qbytes = (in_b + 1.0) * M * K
+        f8_tflops = flops / (f["gemm_ms"] * 1e-3) / 1e12
+        extra["fp8_w8a8"] = dict(
+            gemm_ms=f["gemm_ms"], gemm_tflops=f8_tflops, gemm_frac_fp8_peak=f8_tflops / FP8_MFMA_PEAK_TFLOPS,
+            quantize_ms=f["quantize_ms"], quantize_gbs=f8_qbytes / (f["quantize_ms"] * 1e-3) / 1e9,
+            quantize_frac_hbm=f8_qbytes / (f["quantize_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            step_ms=f["step_ms"], step_tflops=flops / (f["step_ms"] * 1e-3) / 1e12,
+            note="same layer in FP8 E4M3 W8A8 (per-tensor scales; fp8_gemm_dma_kernel on the FP8 MFMA); "
+                 "weights quantized offline; each kernel timed back to back; quantize bytes: read X, "
+                 "write one byte per element")
     value = flops / (step_ms * 1e-3) / 1e12
     config = dict(workload=st["name"], M=M, N=N, K=K, x=cfg["x_dtype"], out=cfg["out"],
                   weights="NVFP4, quantized offline (static)", activations="NVFP4, dynamic, quantized in the step")
@@ -424,6 +455,9 @@ def main():
             sq.append((e0, e1))
         torch.cuda.synchronize()
         st["quantize_static_ms"] = sum(a.elapsed_time(b) for a, b in sq) / len(sq)
+
+    if kind == "linear":
+        measure_fp8(B, st, args.steps)
 
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
