@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--static-scales", action="store_true",
                    help="MoE: static (calibrated) activation scales, h quantized in the gate_up epilogue")
+    p.add_argument("--library-reference", action="store_true",
+                   help="dense: also time the platform's FP8 (torch._scaled_mm) and bf16 (torch.matmul) "
+                        "GEMMs at the same shape, as context")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -170,6 +173,34 @@ def step_dense(B, st, timer=None):
         timer.add("gemm", t1, t2)
 
 
+def library_reference(st, reps):
+    """The platform libraries' GEMMs at the dense shape (context, not part of the path):
+    FP8 E4M3 x E4M3 with unit scales through torch._scaled_mm, and bf16 x bf16 through
+    torch.matmul, on random operands of the workload's shape."""
+    cfg = st["cfg"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    flops = 2.0 * M * N * K
+    out = {}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    a = torch.randn((M, K), generator=gen, device="cuda")
+    b = torch.randn((N, K), generator=gen, device="cuda")
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        one = torch.ones((), device="cuda")
+        ms = _time_ms(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), reps)
+        out["fp8_scaled_mm"] = dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+        del a8, b8
+    except Exception as ex:  # the library call is optional context
+        out["fp8_scaled_mm"] = dict(error=str(ex)[:200])
+    ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16)
+    del a, b
+    ms = _time_ms(lambda: ab @ bb.t(), reps)
+    out["bf16_matmul"] = dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+    out["note"] = "platform GEMM libraries through torch at the same shape; context only"
+    st["library_reference"] = out
+
+
 def report_dense(st, timer, step_ms):
     cfg = st["cfg"]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
@@ -236,14 +267,21 @@ def report_dense(st, timer, step_ms):
         in_b = 2 if cfg["x_dtype"] == "bf16" else 4
         f8_qbytes = (in_b + 1.0) * M * K
         f8_tflops = flops / (f["gemm_ms"] * 1e-3) / 1e12
+        f8_traffic = None
+        if st["name"] == "prefill_8192x5120":
+            f8_traffic = profiled_traffic("fp8_gemm_prefill_8192x5120x25600.md",
+                                          "moe_nvfp4_quantize_amd/csrc/fp8_gemm.hip")
         extra["fp8_w8a8"] = dict(
             gemm_ms=f["gemm_ms"], gemm_tflops=f8_tflops, gemm_frac_fp8_peak=f8_tflops / FP8_MFMA_PEAK_TFLOPS,
+            gemm_traffic=f8_traffic, gemm_algorithmic_bytes=(M * K + N * K) + out_b * M * N,
             quantize_ms=f["quantize_ms"], quantize_gbs=f8_qbytes / (f["quantize_ms"] * 1e-3) / 1e9,
             quantize_frac_hbm=f8_qbytes / (f["quantize_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             step_ms=f["step_ms"], step_tflops=flops / (f["step_ms"] * 1e-3) / 1e12,
             note="same layer in FP8 E4M3 W8A8 (per-tensor scales; fp8_gemm_dma_kernel on the FP8 MFMA); "
                  "weights quantized offline; each kernel timed back to back; quantize bytes: read X, "
                  "write one byte per element")
+    if "library_reference" in st:
+        extra["library_reference"] = st["library_reference"]
     value = flops / (step_ms * 1e-3) / 1e12
     config = dict(workload=st["name"], M=M, N=N, K=K, x=cfg["x_dtype"], out=cfg["out"],
                   weights="NVFP4, quantized offline (static)", activations="NVFP4, dynamic, quantized in the step")
@@ -458,6 +496,8 @@ def main():
 
     if kind == "linear":
         measure_fp8(B, st, args.steps)
+        if args.library_reference:
+            library_reference(st, args.steps)
 
     if args.copy_probe_mib:
         a = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")

@@ -289,16 +289,30 @@ __device__ __forceinline__ float global_from_amax(float amax) {
 
 // ------------------------------------------------------------ two-pass path
 
+// One workgroup per partial (at most 256 per matrix, so as few as one per CU):
+// each thread keeps NU blocks (256 bytes) of loads in flight per iteration.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void amax_partials_kernel(QuantParams p) {
+  constexpr uint32_t NU = 256 / (16 * sizeof(T));
   const uint32_t b = blockIdx.y;
   const T *x = static_cast<const T *>(p.x) + (int64_t)b * p.x_mstride;
-  float m = 0.0f;
-  for (uint32_t u = blockIdx.x * kThreads + threadIdx.x; u < p.units; u += gridDim.x * kThreads) {
+  const uint32_t stride = gridDim.x * kThreads;
+  auto at = [&](uint32_t u) {
     const uint32_t row = p.div_nbpr.div(u);
-    const uint32_t blk = u - row * p.nbpr;
+    return x + (int64_t)row * p.ld + (u - row * p.nbpr) * 16;
+  };
+  float m = 0.0f;
+  uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  for (; (uint64_t)u + (NU - 1) * (uint64_t)stride < p.units; u += NU * stride) {
+    uint32_t w[NU][Raw<T>::W];
+#pragma unroll
+    for (uint32_t i = 0; i < NU; ++i) load_raw<T, VEC, false>(at(u + i * stride), w[i]);
+#pragma unroll
+    for (uint32_t i = 0; i < NU; ++i) m = fmaxf(m, raw_max<T>(w[i]));
+  }
+  for (; u < p.units; u += stride) {
     uint32_t w[Raw<T>::W];
-    load_raw<T, VEC, false>(x + (int64_t)row * p.ld + blk * 16, w);
+    load_raw<T, VEC, false>(at(u), w);
     m = fmaxf(m, raw_max<T>(w));
   }
   m = block_max(m);
