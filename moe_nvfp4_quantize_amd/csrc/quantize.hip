@@ -1,9 +1,15 @@
-// quantize.hip -- dynamic / static two-level NVFP4 quantization on gfx950.
+// quantize.hip -- dynamic / static two-level NVFP4 quantization on gfx950,
+// and the kernels' other modes on the same data path: four-over-six block
+// scales, quantize-dequantize, and FP8 E4M3 per-tensor quantization.
 //
 // Qwen3.8-Flash-Next-NVFP4 page, section "Core: the W4A4 two-level scaling
 // mechanism" (level 1: one E4M3 scale per 16 elements along the last dimension;
 // level 2: one FP32 scale per tensor) and sub-section "The A4 side: dynamic
 // activations" (activations quantized on the fly with the same rule).
+//
+// Every kernel walks x in units of 16 consecutive elements of a row and takes a
+// mode (enum Mode) that decides what a unit becomes; the per-mode encoders sit
+// next to the plain one below.
 //
 // The dynamic global scale needs max|x| over the whole tensor before any block
 // can be encoded.  Two kernels implement that:

@@ -385,21 +385,22 @@ def nvfp4_moe_combine(y, topk_w, inv, out_dtype=torch.bfloat16, out=None, stream
     return out
 
 
-def moe_layer(x, logits, k, w_gate_up, w_down, stream=None, keep=False):
+def moe_layer(x, logits, k, w_gate_up, w_down, stream=None, keep=False, inter_dtype=torch.float32):
     """The routed-expert layer as a sequence of library calls.
 
     x bf16/f32 [T, H]; w_gate_up and w_down are quantized expert stacks
-    (q, s, g) for [E, 2I, H] and [E, H, I].  Returns the bf16 output, or with
-    ``keep=True`` a dict of every intermediate.
+    (q, s, g) for [E, 2I, H] and [E, H, I].  ``inter_dtype`` (float32 or
+    bfloat16) is the storage type of the intermediates h and y.  Returns the
+    bf16 output, or with ``keep=True`` a dict of every intermediate.
     """
     T = x.shape[0]
     r = nvfp4_moe_route(logits, k, stream=stream)
     R = T * k
     xq = nvfp4_quantize(x, stream=stream)
     h = nvfp4_moe_grouped_gemm(xq, r["src_row"], r["offsets"], R, w_gate_up,
-                               epilogue=NVFP4_EPI_SILU_GATE, out_dtype=torch.float32, stream=stream)
+                               epilogue=NVFP4_EPI_SILU_GATE, out_dtype=inter_dtype, stream=stream)
     hq = nvfp4_quantize(h, stream=stream)
-    y = nvfp4_moe_grouped_gemm(hq, None, r["offsets"], R, w_down, out_dtype=torch.float32,
+    y = nvfp4_moe_grouped_gemm(hq, None, r["offsets"], R, w_down, out_dtype=inter_dtype,
                                stream=stream)
     out = nvfp4_moe_combine(y, r["topk_w"], r["inv"], stream=stream)
     if keep:

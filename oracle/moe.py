@@ -25,12 +25,16 @@ Readings taken where the pages are silent:
 * one global scale per quantize call: the token activations X before
   permutation (one tensor), h over all routed rows (one tensor), and each expert's
   gate_up and down matrices (one tensor each);
-* the combine sums ``w[t, j] * y[row(t, j)]`` over slots j = 0..k-1 in order.
+* the combine sums ``w[t, j] * y[row(t, j)]`` over slots j = 0..k-1 in order;
+* the intermediates h and y are stored either as float32 or, as serving engines
+  keep activations, in bfloat16 (rounded to nearest even from float32); the
+  quantizer of h reads the stored h and the combine the stored y.
 """
 
 import numpy as np
 
 from .nvfp4 import quantize, dequantize
+from .qdq import round_to_bf16
 
 
 def topk(logits, k):
@@ -132,22 +136,31 @@ def quantize_experts(w):
     return np.stack(qs), np.stack(ss), np.array(gs, dtype=np.float32)
 
 
-def moe_forward(x, logits, k, wgu, wd):
+def moe_forward(x, logits, k, wgu, wd, inter="f32"):
     """Whole routed-expert layer, every stage returned.
 
     ``x`` float32 [T, H] (bf16 widened), ``logits`` float32 [T, E], ``wgu`` a
     quantized stack ``(q, s, g)`` for gate_up [E, 2I, H], ``wd`` for down [E, H, I].
     The intermediate h is rounded to float32 before its quantization (the
-    activation fed to a quantized linear is a float32 tensor).
+    activation fed to a quantized linear is a float32 tensor).  ``inter="bf16"``
+    stores h and y in bfloat16 instead: h and y are then rounded once more, from
+    float32 to bfloat16, before the quantizer and the combine read them; the
+    returned ``h`` and ``y`` are the stored values.
     """
+    if inter not in ("f32", "bf16"):
+        raise ValueError("inter must be 'f32' or 'bf16'")
     E = np.asarray(logits).shape[1]
     ids, w = route(logits, k)
     offsets, src_row, inv = permute(ids, E)
     xq = quantize(x)
     gu = grouped_gemm(*xq, src_row, offsets, *wgu)
     h = silu_gate(gu)
+    if inter == "bf16":
+        h = round_to_bf16(h.astype(np.float32)).astype(np.float64)
     hq = quantize(h.astype(np.float32))
     y = grouped_gemm(*hq, None, offsets, *wd)
+    if inter == "bf16":
+        y = round_to_bf16(y.astype(np.float32)).astype(np.float64)
     out = combine(y, w, inv)
     return dict(topk_ids=ids, topk_w=w, offsets=offsets, src_row=src_row, inv=inv,
                 xq=xq, gu=gu, h=h, hq=hq, y=y, out=out)

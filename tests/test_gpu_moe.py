@@ -253,28 +253,30 @@ def test_combine(B, T, k, H, y_bf16):
 
 @pytest.mark.parametrize("T,E,k,H,I,hot", [(256, 16, 4, 512, 256, 0), (512, 64, 8, 256, 128, 4),
                                            (96, 8, 1, 256, 64, 0)])
-def test_layer_end_to_end(B, T, E, k, H, I, hot):
+@pytest.mark.parametrize("inter", ["f32", "bf16"])
+def test_layer_end_to_end(B, T, E, k, H, I, hot, inter):
     inp = W.moe_inputs("moe_e512_top10", device="cuda", T=T, E=E, k=k, H=H, I=I, hot=hot)
     wgu = B.nvfp4_quantize_batched(inp["w_gate_up"])
     wd = B.nvfp4_quantize_batched(inp["w_down"])
-    res = B.moe_layer(inp["x"], inp["logits"], k, wgu, wd, keep=True)
+    res = B.moe_layer(inp["x"], inp["logits"], k, wgu, wd, keep=True,
+                      inter_dtype=torch.bfloat16 if inter == "bf16" else torch.float32)
     torch.cuda.synchronize()
     qgu = OM.quantize_experts(_np(inp["w_gate_up"].float()))
     qd = OM.quantize_experts(_np(inp["w_down"].float()))
     # the GPU's offline weight quantization is bit-exact
     for got, ref in zip(wgu + wd, qgu + qd):
         np.testing.assert_array_equal(_np(got), ref)
-    ref = OM.moe_forward(_np(inp["x"].float()), _np(inp["logits"]), k, qgu, qd)
+    ref = OM.moe_forward(_np(inp["x"].float()), _np(inp["logits"]), k, qgu, qd, inter=inter)
     np.testing.assert_array_equal(_np(res["topk_ids"]), ref["topk_ids"])
     np.testing.assert_array_equal(_np(res["src_row"]), ref["src_row"])
     for got, want in zip(res["xq"], ref["xq"]):
         np.testing.assert_array_equal(_np(got).reshape(np.shape(want)), want)
-    h_err = OG.rel_fro_error(_np(res["h"]).astype(np.float64), ref["h"])
+    h_err = OG.rel_fro_error(_np(res["h"].float()).astype(np.float64), ref["h"])
     hq_codes = OQ.unpack_codes(_np(res["hq"][0]))
     same = np.mean(hq_codes == OQ.unpack_codes(ref["hq"][0]))
-    y_err = OG.rel_fro_error(_np(res["y"]).astype(np.float64), ref["y"])
+    y_err = OG.rel_fro_error(_np(res["y"].float()).astype(np.float64), ref["y"])
     out_err = OG.rel_fro_error(_np(res["out"].float()), _bf16_round(ref["out"]))
-    print(f"[moe] e2e T={T} E={E} k={k}: h {h_err:.2e}, hq codes equal {same:.5f}, y {y_err:.2e}, "
+    print(f"[moe] e2e T={T} E={E} k={k} {inter}: h {h_err:.2e}, hq codes equal {same:.5f}, y {y_err:.2e}, "
           f"out {out_err:.2e}", flush=True)
     assert h_err <= TOL
     assert same >= 0.999

@@ -204,3 +204,29 @@ def test_grouped_gemm_empty_experts_and_gather():
     y = M.grouped_gemm(*a, src, offsets, *w)
     ref = Q.dequantize(*a)[src] @ Q.dequantize(w[0][1], w[1][1], w[2][1]).T
     np.testing.assert_allclose(y, ref, rtol=1e-14)
+
+
+def test_bf16_intermediates_round_through_torch_bfloat16():
+    """With inter="bf16" the stored h and y are torch's bfloat16 casts of the
+    float32 values of the float32 path's stages, and the output is their combine."""
+    import torch
+    rng = np.random.default_rng(9)
+    T, H, I, E, k = 24, 64, 32, 4, 2
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wgu, wd = _experts(rng, E, I, H)
+    qgu, qd = M.quantize_experts(wgu), M.quantize_experts(wd)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ref = M.moe_forward(x, logits, k, qgu, qd)
+    got = M.moe_forward(x, logits, k, qgu, qd, inter="bf16")
+
+    def bf(v):
+        return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(got["h"], bf(ref["h"]))
+    hq = Q.quantize(bf(ref["h"]).astype(np.float32))
+    for a, b in zip(got["hq"], hq):
+        np.testing.assert_array_equal(a, b)
+    y = M.grouped_gemm(*hq, None, ref["offsets"], *qd)
+    np.testing.assert_array_equal(got["y"], bf(y))
+    np.testing.assert_array_equal(got["out"], M.combine(bf(y), ref["topk_w"], ref["inv"]))
+    with pytest.raises(ValueError):
+        M.moe_forward(x, logits, k, qgu, qd, inter="f16")
