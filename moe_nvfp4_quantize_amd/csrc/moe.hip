@@ -13,10 +13,11 @@
 //              k selected logits.
 //   2. count:  one wave per group of 64 tokens; LDS bit masks mask[e] (bit L =
 //              token L of the group picked e), counts[g][e] = popcount.
-//   3. scan:   one workgroup; exclusive prefix of counts in (expert, group)
-//              order -> base[g][e] and expert_offsets.
+//   3. scan:   one workgroup; per expert, the exclusive prefix of its counts
+//              over the groups -> base[g][e] (in place), and the exclusive
+//              prefix of the experts' totals -> expert_offsets.
 //   4. place:  one wave per group; the row of (token L, slot j) with expert e is
-//              base[g][e] + popcount(mask[e] & bits below L).
+//              expert_offsets[e] + base[g][e] + popcount(mask[e] & bits below L).
 #include "nvfp4_common.hpp"
 #include "nvfp4_format.hpp"
 #include "nvfp4_kernels.hpp"
@@ -27,8 +28,10 @@ namespace {
 
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
-constexpr int kPerLane = kMaxE / 64;
+constexpr int kMaxPerLane = kMaxE / 64;
 
+// PL = logits per lane (E <= 64 PL)
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, uint32_t T,
                                                    uint32_t E, uint32_t k, int32_t *__restrict__ ids,
                                                    float *__restrict__ w) {
@@ -36,9 +39,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
   const uint32_t t = blockIdx.x * 4 + threadIdx.x / 64;
   if (t >= T) return;
   const float *row = logits + (int64_t)t * E;
-  float v[kPerLane];
+  float v[PL];
 #pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     const uint32_t e = lane + 64u * i;
     v[i] = e < E ? row[e] : -INFINITY;
   }
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     float bv = -INFINITY;
     int32_t be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const uint32_t e = lane + 64u * i;
       if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && (int32_t)e < be))) {
         bv = v[i];
@@ -101,39 +104,50 @@ __global__ __launch_bounds__(64) void count_kernel(const int32_t *ids, uint32_t 
   for (uint32_t e = threadIdx.x; e < E; e += 64) counts[(int64_t)g * E + e] = __popcll(mask[e]);
 }
 
-// one workgroup of 1024 threads; counts[g][e] -> base[g][e] (in place) with the
-// exclusive prefix taken in (e, g) order; offsets[e] = base[0][e], offsets[E] = R
+// One workgroup of 1024 threads.  Thread e < E walks expert e's column of
+// counts[g][e] (coalesced across the threads) and replaces it in place by its
+// exclusive prefix over g; the column totals are then scanned over e into
+// offsets (offsets[e] = first row of expert e, offsets[E] = R).  The routed row
+// of group g's first token with expert e is offsets[e] + counts[g][e].
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t *counts, uint32_t G, uint32_t E,
                                                     int32_t *offsets) {
   __shared__ int32_t part[1024];
-  const uint32_t n = G * E;
-  const uint32_t per = (n + 1023) / 1024;
-  const uint32_t lo = threadIdx.x * per, hi = min(lo + per, n);
-  // element i of the (e, g) order is counts[g][e] with e = i / G, g = i % G
-  int32_t s = 0;
-  for (uint32_t i = lo; i < hi; ++i) s += counts[(int64_t)(i % G) * E + i / G];
-  part[threadIdx.x] = s;
+  const uint32_t e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    uint32_t g = 0;
+    for (; g + 8 <= G; g += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = counts[(int64_t)(g + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        counts[(int64_t)(g + i) * E + e] = run;
+        run += c[i];
+      }
+    }
+    for (; g < G; ++g) {
+      const int32_t c = counts[(int64_t)g * E + e];
+      counts[(int64_t)g * E + e] = run;
+      run += c;
+    }
+  }
+  part[e] = run;
   __syncthreads();
   for (uint32_t off = 1; off < 1024; off <<= 1) {
-    int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    const int32_t v = e >= off ? part[e - off] : 0;
     __syncthreads();
-    part[threadIdx.x] += v;
+    part[e] += v;
     __syncthreads();
   }
-  int32_t run = part[threadIdx.x] - s;
-  for (uint32_t i = lo; i < hi; ++i) {
-    int32_t *c = counts + (int64_t)(i % G) * E + i / G;
-    const int32_t cnt = *c;
-    *c = run;
-    if (i % G == 0) offsets[i / G] = run;
-    run += cnt;
-  }
-  if (threadIdx.x == 1023) offsets[E] = part[1023];
+  if (e < E) offsets[e] = part[e] - run;
+  if (e == 1023) offsets[E] = part[1023];
 }
 
 __global__ __launch_bounds__(64) void place_kernel(const int32_t *ids, uint32_t T, uint32_t E,
                                                    uint32_t k, const int32_t *base,
-                                                   int32_t *src_row, int32_t *inv) {
+                                                   const int32_t *offsets, int32_t *src_row,
+                                                   int32_t *inv) {
   __shared__ unsigned long long mask[kMaxE];
   const uint32_t g = blockIdx.x;
   build_masks(mask, ids, T, E, k, g);
@@ -143,15 +157,49 @@ __global__ __launch_bounds__(64) void place_kernel(const int32_t *ids, uint32_t 
   const unsigned long long below = (1ull << lane) - 1ull;
   for (uint32_t j = 0; j < k; ++j) {
     const int32_t e = ids[(int64_t)t * k + j];
-    const int32_t r = base[(int64_t)g * E + e] + __popcll(mask[e] & below);
+    const int32_t r = offsets[e] + base[(int64_t)g * E + e] + __popcll(mask[e] & below);
     src_row[r] = (int32_t)t;
     inv[(int64_t)t * k + j] = r;
   }
 }
 
-// out[t][h] = sum_j w[t][j] * y[inv[t][j]][h]; one workgroup per token, 4
-// consecutive h per thread.
-template <typename YT, typename OT>
+// out[t][h] = sum_j w[t][j] * y[inv[t][j]][h], slots in order, one product and
+// one float32 addition per slot (no fused multiply-add); one workgroup per token.
+// VEC (H % 8 == 0, 16-byte aligned y and out): each thread owns 8 consecutive h
+// and loads them 16 (bf16) or 32 (f32) bytes at a time, four slots' loads in
+// flight before they are summed; otherwise one h per thread.
+template <typename YT>
+__device__ __forceinline__ void load8(const YT *p, float v[8]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (sizeof(YT) == 4) {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(p), b = *reinterpret_cast<const u32x4 *>(p + 4);
+    for (int i = 0; i < 4; ++i) {
+      v[i] = u2f(a[i]);
+      v[4 + i] = u2f(b[i]);
+    }
+  } else {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(p);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(a[i]);
+      v[2 * i + 1] = bf16_hi(a[i]);
+    }
+  }
+}
+
+template <typename OT>
+__device__ __forceinline__ void store8(OT *p, const float v[8]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (sizeof(OT) == 4) {
+    *reinterpret_cast<u32x4 *>(p) = (u32x4){f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
+    *reinterpret_cast<u32x4 *>(p + 4) = (u32x4){f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])};
+  } else {
+    u32x4 o;
+    for (int i = 0; i < 4; ++i) o[i] = float_to_bf16_bits(v[2 * i]) | (float_to_bf16_bits(v[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4 *>(p) = o;
+  }
+}
+
+template <typename YT, typename OT, bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y,
                                                       const float *__restrict__ w,
                                                       const int32_t *__restrict__ inv, uint32_t k,
@@ -164,21 +212,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y,
     ws[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (uint32_t h = threadIdx.x; h < H; h += 256) {
-    float acc = 0.0f;
-    for (uint32_t j = 0; j < k; ++j) {
-      float v;
-      if constexpr (sizeof(YT) == 4)
-        v = y[(int64_t)rows[j] * H + h];
-      else
-        v = u2f((uint32_t)y[(int64_t)rows[j] * H + h] << 16);
-      acc += ws[j] * v;
+  if constexpr (VEC) {
+    for (uint32_t h = threadIdx.x * 8; h < H; h += 256 * 8) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint32_t j = 0;
+      for (; j + 4 <= k; j += 4) {
+        float v[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load8<YT>(y + (int64_t)rows[j + q] * H + h, v[q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += ws[j + q] * v[q][i];
+      }
+      for (; j < k; ++j) {
+        float v[8];
+        load8<YT>(y + (int64_t)rows[j] * H + h, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += ws[j] * v[i];
+      }
+      store8<OT>(out + (int64_t)t * H + h, acc);
     }
-    if constexpr (sizeof(OT) == 4)
-      out[(int64_t)t * H + h] = acc;
-    else
-      out[(int64_t)t * H + h] = (OT)float_to_bf16_bits(acc);
+  } else {
+    for (uint32_t h = threadIdx.x; h < H; h += 256) {
+      float acc = 0.0f;
+      for (uint32_t j = 0; j < k; ++j) {
+        float v;
+        if constexpr (sizeof(YT) == 4)
+          v = y[(int64_t)rows[j] * H + h];
+        else
+          v = u2f((uint32_t)y[(int64_t)rows[j] * H + h] << 16);
+        acc += ws[j] * v;
+      }
+      if constexpr (sizeof(OT) == 4)
+        out[(int64_t)t * H + h] = acc;
+      else
+        out[(int64_t)t * H + h] = (OT)float_to_bf16_bits(acc);
+    }
   }
+}
+
+template <typename YT, typename OT>
+hipError_t launch_combine_t(const void *y, const float *w, const int32_t *inv, int64_t T, int32_t k,
+                            int64_t H, void *out, hipStream_t stream) {
+  const bool vec = H % 8 == 0 && ((uintptr_t)y & 15u) == 0 && ((uintptr_t)out & 15u) == 0;
+  if (vec)
+    combine_kernel<YT, OT, true><<<(uint32_t)T, 256, 0, stream>>>((const YT *)y, w, inv, (uint32_t)k,
+                                                                  (uint32_t)H, (OT *)out);
+  else
+    combine_kernel<YT, OT, false><<<(uint32_t)T, 256, 0, stream>>>((const YT *)y, w, inv, (uint32_t)k,
+                                                                   (uint32_t)H, (OT *)out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -194,8 +278,16 @@ hipError_t launch_route(const float *logits, int64_t T, int32_t E, int32_t k, in
   const uint32_t G = (uint32_t)((T + 63) / 64);
   int32_t *counts = static_cast<int32_t *>(workspace);
   if (T > 0) {
-    topk_kernel<<<(uint32_t)((T + 3) / 4), 256, 0, stream>>>(logits, (uint32_t)T, (uint32_t)E,
-                                                              (uint32_t)k, topk_ids, topk_w);
+    const uint32_t grid = (uint32_t)((T + 3) / 4);
+    if (E <= 128)
+      topk_kernel<2><<<grid, 256, 0, stream>>>(logits, (uint32_t)T, (uint32_t)E, (uint32_t)k, topk_ids, topk_w);
+    else if (E <= 256)
+      topk_kernel<4><<<grid, 256, 0, stream>>>(logits, (uint32_t)T, (uint32_t)E, (uint32_t)k, topk_ids, topk_w);
+    else if (E <= 512)
+      topk_kernel<8><<<grid, 256, 0, stream>>>(logits, (uint32_t)T, (uint32_t)E, (uint32_t)k, topk_ids, topk_w);
+    else
+      topk_kernel<kMaxPerLane><<<grid, 256, 0, stream>>>(logits, (uint32_t)T, (uint32_t)E, (uint32_t)k, topk_ids,
+                                                      topk_w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     count_kernel<<<G, 64, 0, stream>>>(topk_ids, (uint32_t)T, (uint32_t)E, (uint32_t)k, counts);
@@ -205,30 +297,18 @@ hipError_t launch_route(const float *logits, int64_t T, int32_t E, int32_t k, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   place_kernel<<<G, 64, 0, stream>>>(topk_ids, (uint32_t)T, (uint32_t)E, (uint32_t)k, counts,
-                                     src_row, inv);
+                                     offsets, src_row, inv);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const void *y, bool y_bf16, const float *w, const int32_t *inv, int64_t T,
                           int32_t k, int64_t H, void *out, bool out_bf16, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((uint32_t)T);
-  if (y_bf16) {
-    if (out_bf16)
-      combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, stream>>>(
-          (const uint16_t *)y, w, inv, k, (uint32_t)H, (uint16_t *)out);
-    else
-      combine_kernel<uint16_t, float><<<grid, 256, 0, stream>>>((const uint16_t *)y, w, inv, k,
-                                                                (uint32_t)H, (float *)out);
-  } else {
-    if (out_bf16)
-      combine_kernel<float, uint16_t><<<grid, 256, 0, stream>>>((const float *)y, w, inv, k,
-                                                                (uint32_t)H, (uint16_t *)out);
-    else
-      combine_kernel<float, float><<<grid, 256, 0, stream>>>((const float *)y, w, inv, k,
-                                                             (uint32_t)H, (float *)out);
-  }
-  return hipGetLastError();
+  if (y_bf16)
+    return out_bf16 ? launch_combine_t<uint16_t, uint16_t>(y, w, inv, T, k, H, out, stream)
+                    : launch_combine_t<uint16_t, float>(y, w, inv, T, k, H, out, stream);
+  return out_bf16 ? launch_combine_t<float, uint16_t>(y, w, inv, T, k, H, out, stream)
+                  : launch_combine_t<float, float>(y, w, inv, T, k, H, out, stream);
 }
 
 }  // namespace nvfp4
