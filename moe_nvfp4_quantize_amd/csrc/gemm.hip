@@ -402,7 +402,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
 //    LDS), so no registers hold staged data and no LDS store instructions run.
 //  * Codes: three stages of one K step (128 elements: 64 bytes per row),
-//    fetched two steps ahead.  Scales: two chunks of eight K steps (64 bytes per
+//    fetched two steps ahead (four stages, three steps ahead, for 128-row
+//    tiles).  Scales: two chunks of eight K steps (64 bytes per
 //    row), so that a transfer reads 64 contiguous bytes of a row instead of 8;
 //    the next chunk is fetched during the first four steps of the current one.
 //  * Each step issues the same ten transfers (extra ones reload data that is
@@ -424,8 +425,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   static_assert(!QOUT || (SILU && sizeof(OutT) == 4), "NVFP4 output: SiLU-gate epilogue, f32 staging");
   // transfers (64 lanes x 16 bytes) per operand: per code stage, and per scale chunk
   constexpr int TA = BM / 64, TB = BN / 64, TN = TA + TB;
-  // code stages: [A BM rows x 64 B][B 256 rows x 64 B], three of them
-  constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = 3;
+  // code stages: [A BM rows x 64 B][B 256 rows x 64 B], fetched AHEAD steps
+  // ahead: four stages for 128-row tiles (skinny products stream their weights
+  // from HBM, so the fetch has to run further ahead; 144 KB of LDS), three
+  // otherwise (a fourth would not fit)
+  constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = BM == 128 ? 4 : 3;
+  constexpr int AHEAD = NSTAGE - 1;
   // scale chunks: the scales of SC_STEPS K steps, [A BM rows x 64 B][B ...], two of them
   constexpr int SC_STEPS = 8, SC_B = BM * 64, SC_CHUNK = (BM + BN) * 64;
   constexpr int OFF_SC = NSTAGE * CODE_STAGE;
@@ -802,23 +807,27 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // step ks of tile i.  Software pipeline: while the MFMAs of sub-step t run,
   // the operands of sub-step t + 1 are decoded; the next step's first half is
   // read from LDS while this step's second half is multiplied.  Codes are
-  // fetched two steps ahead (across a tile boundary: the next tile's first
+  // fetched AHEAD steps ahead (across a tile boundary: the next tile's first
   // steps); scale chunk c + 1 (or the next tile's chunk 0) during the first
   // four steps of chunk c.  Every step issues TN + 2 transfers (near the end
   // the last step's codes again, into a stage nobody reads any more; outside
   // the first four steps of a chunk the current chunk's scales again,
   // rewriting identical bytes), so at the mid-step barrier one wait count
-  // leaves exactly this step's own transfers in flight.  At the last step of a
+  // leaves in flight only what was issued after the fetch of the next step.  At the last step of a
   // tile its epilogue runs, behind the already issued transfers of the next.
   uint32_t nrow0 = row0, ntile_n = tile_n;  // the tile after the current one
   if (my_tiles > 1) origin(1, &nrow0, &ntile_n);
 #pragma unroll
   for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j % TA, j);
+  // steps 0 .. AHEAD - 1 (a short single tile reloads its last step into the
+  // stages past it, which nobody reads; a walk of several tiles has at least 8
+  // steps per tile)
 #pragma unroll
-  for (int q = 0; q < TN; ++q) issue_code(0, 0, a_base(row0), b_base(tile_n), q);
+  for (int st = 0; st < AHEAD; ++st)
 #pragma unroll
-  for (int q = 0; q < TN; ++q) issue_code(1, 1, a_base(row0), b_base(tile_n), q);
-  wait_vm<TN>();
+    for (int q = 0; q < TN; ++q)
+      issue_code(st, min((uint32_t)st, nsteps - 1), a_base(row0), b_base(tile_n), q);
+  wait_vm<(AHEAD - 1) * TN>();
   uint32_t g = 0;
   for (uint32_t ti = 0; ti < my_tiles; ++ti) {
     // the tile's first step: its data landed before the previous barrier
@@ -835,8 +844,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     half8v av[2][FM], bv[2][FN];
     decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
     for (uint32_t ks = 0; ks < nsteps; ++ks, ++g) {
-      // codes of global step g + 2
-      uint32_t fks = ks + 2, far_ = a_base(row0), fbc = b_base(tile_n);
+      // codes of global step g + AHEAD
+      uint32_t fks = ks + AHEAD, far_ = a_base(row0), fbc = b_base(tile_n);
       if (fks >= nsteps) {
         if (ti + 1 < my_tiles) {
           fks -= nsteps;
@@ -869,14 +878,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
         else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
 #pragma unroll
-        for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + 2, fks, far_, fbc, q);
+        for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
         if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, (part % 4) % TA, part % 4);
         if (t == 0) interleave(std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
         if (t == 1) interleave(std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
         if (t == 2) interleave(std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
         if (t == 3) interleave(std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
       }
-      wait_vm<TN + 2>();
+      // step g + 1 has landed: at most the transfers issued since the
+      // fetch of step g + 1 (the last AHEAD - 1 steps' codes, and scales) remain
+      wait_vm<(AHEAD - 1) * TN + 2>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
