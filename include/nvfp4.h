@@ -30,7 +30,8 @@
  *     results.  Nothing is printed and nothing aborts.
  *   - Calls on one stream are ordered; calls that share output or workspace
  *     buffers on different streams race.  The library keeps no global state
- *     other than a per-device cache of the architecture check.
+ *     other than per-device caches of the architecture check and the compute
+ *     unit count.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -171,8 +172,9 @@ nvfp4_status nvfp4_quantize_4over6(const void *x, nvfp4_dtype x_type,
  * once in the epilogue; the result is rounded to c_type.
  * M, N >= 0; K > 0 and a multiple of 16.  c is [M][ldc] of c_type, ldc >= N.
  * a_g, b_g: device floats (read by the kernel; no host synchronization).
- * Faster paths need K % 128 == 0 and 16-byte aligned q rows; other shapes are
- * handled by a general path with the same results.
+ * The fastest path needs K % 256 == 0 and 16-byte aligned q and s; K % 128
+ * == 0 with aligned rows takes a vector-load path, other shapes a general
+ * path; all give results within the same bound.
  * ---------------------------------------------------------------------- */
 nvfp4_status nvfp4_gemm(const uint8_t *a_q, const uint8_t *a_s, const float *a_g,
                         const uint8_t *b_q, const uint8_t *b_s, const float *b_g,

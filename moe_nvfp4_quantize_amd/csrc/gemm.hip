@@ -979,16 +979,7 @@ bool dma_ok(const GemmParams &p, uint64_t a_rows) {
 // workgroup's tiles on one XCD.
 uint32_t persistent_grid(const GemmParams &p, uint32_t tiles) {
   if ((p.K / 128) % 8 != 0) return tiles;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return tiles;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      return tiles;
-    cus[dev] = n;
-  }
-  const uint32_t g = (uint32_t)cus[dev] & ~7u;
+  const uint32_t g = device_cu_count() & ~7u;
   return g == 0 || tiles <= g ? tiles : g;
 }
 

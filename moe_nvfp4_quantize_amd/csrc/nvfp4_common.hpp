@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
 
 // Unsigned 32-bit division by a run-time constant d >= 1 through a multiply and
@@ -41,6 +43,23 @@ __device__ __forceinline__ float block_max(float v) {
   const int nw = blockDim.x >> 6;
   float r = lane < nw ? red[lane] : 0.0f;
   return wave_max(r);
+}
+
+// Compute units of the current device, cached per device (host; 0 when the
+// query fails).  The cache is written with relaxed atomics: concurrent first
+// calls store the same value.
+inline uint32_t device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+    cache[dev].store(n, std::memory_order_relaxed);
+    v = n;
+  }
+  return v > 0 ? (uint32_t)v : 0u;
 }
 
 // ------------------------------------------------------------ GEMM helpers

@@ -494,19 +494,8 @@ hipError_t launch_two_pass(const QuantParams &p, uint32_t batch, hipStream_t str
   return hipGetLastError();
 }
 
-// Number of CUs of the current device (one resident workgroup fits per CU),
-// cached per device.
-uint32_t resident_capacity_wgs() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = cus > 0 ? cus : -1;
-  }
-  return cached[dev] > 0 ? (uint32_t)cached[dev] : 0u;
-}
+// Resident workgroups a launch may count on: one per CU.
+uint32_t resident_capacity_wgs() { return device_cu_count(); }
 
 template <typename T, bool VEC, int U, int NT, int MODE>
 hipError_t launch_resident_u(const QuantParams &p, ResidentState *st, uint32_t G, hipStream_t stream) {
