@@ -614,10 +614,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   const uint32_t l32 = lane % 32, lh = lane / 32;
   // LDS byte offsets of this lane's fragment rows: codes (inside a stage) and
   // scales (inside a chunk, without the step's piece)
+  // A fragment i of wave half wm holds tile rows (2 i + wm) * 32 .. + 31: the
+  // 32-row groups alternate between the two halves, so that a tile whose
+  // rows end early leaves both halves about the same work
   uint32_t offA[FM][2], offB[FN][2], rowSA[FM], rowSB[FN], swA[FM], swB[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const uint32_t r = wm * WM + i * 32 + l32;
+    const uint32_t r = (2 * i + wm) * 32 + l32;
 #pragma unroll
     for (int h = 0; h < 2; ++h) offA[i][h] = r * 64 + (((2 * lh + h) ^ swz(r)) * 16);
     rowSA[i] = r * 64 + lh * 4;
@@ -641,27 +644,33 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // fragments of half h of the code stage of global step g
-  auto read_half = [&](uint32_t g, int h, u32x4 *xa, u32x4 *xb) {
+  // (helpers take F, the number of this wave's A fragments that hold rows of
+  // the tile: 32-row groups past the last row are not read, decoded or
+  // multiplied)
+  auto read_half = [&](auto f_tag, uint32_t g, int h, u32x4 *xa, u32x4 *xb) {
+    constexpr int F = decltype(f_tag)::value;
     const uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
+    for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
   };
   // scale dword of K step ks held in global chunk gc: piece (ks % 8) / 2 of
   // the row's 64 bytes, half ks % 2
-  auto read_scales = [&](uint32_t gc, uint32_t ks, uint32_t *xa, uint32_t *xb) {
+  auto read_scales = [&](auto f_tag, uint32_t gc, uint32_t ks, uint32_t *xa, uint32_t *xb) {
+    constexpr int F = decltype(f_tag)::value;
     const uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + (ks % 2) * 8;
     const uint32_t q = (ks % SC_STEPS) / 2;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
+    for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
 #pragma unroll
     for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const uint32_t *>(st + rowSB[j] + ((q ^ swB[j]) * 16));
   };
   // scale pairs of one step: block b of the lane's four is pair b % 2, element b / 2
-  auto pairs = [&](const uint32_t *ya, const uint32_t *yb, half2v (*pa)[2], half2v (*pb)[2]) {
+  auto pairs = [&](auto f_tag, const uint32_t *ya, const uint32_t *yb, half2v (*pa)[2], half2v (*pb)[2]) {
+    constexpr int F = decltype(f_tag)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < F; ++i) {
       pa[i][0] = scale_pair(ya[i]);
       pa[i][1] = scale_pair(ya[i] >> 8);
     }
@@ -673,26 +682,29 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   };
   // operands of MFMA sub-step t (0..7) of a K step: dword t % 4 of the
   // half-t/4 fragments, block b = t / 2 of the lane's four
-  auto decode_step = [&](int t, const u32x4 *xa, const u32x4 *xb, half2v (*pa)[2],
+  auto decode_step = [&](auto f_tag, int t, const u32x4 *xa, const u32x4 *xb, half2v (*pa)[2],
                          half2v (*pb)[2], half8v *oa8, half8v *ob8) {
+    constexpr int F = decltype(f_tag)::value;
     const int b = t / 2;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) oa8[i] = decode8(xa[i][t % 4], pa[i][b % 2][b / 2]);
+    for (int i = 0; i < F; ++i) oa8[i] = decode8(xa[i][t % 4], pa[i][b % 2][b / 2]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) ob8[j] = decode8(xb[j][t % 4], pb[j][b % 2][b / 2]);
   };
-  auto mfmas = [&](const half8v *oa8, const half8v *ob8) {
+  auto mfmas = [&](auto f_tag, const half8v *oa8, const half8v *ob8) {
+    constexpr int F = decltype(f_tag)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < F; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa8[i], ob8[j], acc[i][j], 0, 0, 0);
   };
   // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), FM * FN
   // times; NV memory transfers spread evenly
-  auto interleave = [&](auto nv_tag) {
-    constexpr int NV = decltype(nv_tag)::value, NM = FM * FN;
-    constexpr int VPM = (8 * (FM + FN) + NM - 1) / NM;
+  auto interleave = [&](auto f_tag, auto nv_tag) {
+    constexpr int F = decltype(f_tag)::value;
+    constexpr int NV = decltype(nv_tag)::value, NM = F * FN;
+    constexpr int VPM = (8 * (F + FN) + NM - 1) / NM;
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -714,11 +726,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr int RPP = 4 * 16 * ROW_BYTES <= CODE_STAGE ? 16 : 8;  // rows per pass
   static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
-  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn) {
+  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf) {
     uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
     const uint32_t col0 = tn * BN_OUT + wn * WN_OUT;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if ((uint32_t)i >= nf) break;  // rows past the tile's end: nothing to write
 #pragma unroll
       for (int ps = 0; ps < 32 / RPP; ++ps) {
 #pragma unroll
@@ -740,7 +753,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
-        const uint32_t rbase = r0 + wm * WM + i * 32 + ps * RPP;
+        const uint32_t rbase = r0 + (2 * i + wm) * 32 + ps * RPP;
         if constexpr (QOUT) {
           // NVFP4 output with the static global scale: one 16-element block per
           // lane (RPP rows x ROW_ELEMS / 16 blocks), the quantizer's arithmetic
@@ -830,19 +843,30 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   wait_vm<(AHEAD - 1) * TN>();
   uint32_t g = 0;
   for (uint32_t ti = 0; ti < my_tiles; ++ti) {
+    // this wave's A fragments that hold rows of the tile
+    const uint32_t rows_in = min(row_end - min(row0, row_end), (uint32_t)BM);
+    const uint32_t groups = (rows_in + 31) / 32;
+    const uint32_t nf = groups > wm ? min((groups - wm + 1) / 2, (uint32_t)FM) : 0u;
+    auto run = [&](auto f_tag) {
+    constexpr int F = decltype(f_tag)::value;
+    const auto ft = f_tag;
     // the tile's first step: its data landed before the previous barrier
     // (fetched during the previous tile), or just above
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     u32x4 fa[FM], fb[FN];
     uint32_t sa[FM], sb[FN];
-    read_half(g, 0, fa, fb);
-    read_scales(ti * cpt, 0, sa, sb);
+    if constexpr (F > 0) {
+      read_half(ft, g, 0, fa, fb);
+      read_scales(ft, ti * cpt, 0, sa, sb);
+    }
     wait_lgkm0();
     half2v spa[FM][2], spb[FN][2];
-    pairs(sa, sb, spa, spb);
     half8v av[2][FM], bv[2][FN];
-    decode_step(0, fa, fb, spa, spb, av[0], bv[0]);
+    if constexpr (F > 0) {
+      pairs(ft, sa, sb, spa, spb);
+      decode_step(ft, 0, fa, fb, spa, spb, av[0], bv[0]);
+    }
     for (uint32_t ks = 0; ks < nsteps; ++ks, ++g) {
       // codes of global step g + AHEAD
       uint32_t fks = ks + AHEAD, far_ = a_base(row0), fbc = b_base(tile_n);
@@ -870,20 +894,24 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
       }
       u32x4 ha[FM], hb[FN];
-      read_half(g, 1, ha, hb);
+      if constexpr (F > 0) read_half(ft, g, 1, ha, hb);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        mfmas(av[t & 1], bv[t & 1]);
-        if (t < 3) decode_step(t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
-        else decode_step(4, ha, hb, spa, spb, av[0], bv[0]);
+        if constexpr (F > 0) {
+          mfmas(ft, av[t & 1], bv[t & 1]);
+          if (t < 3) decode_step(ft, t + 1, fa, fb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+          else decode_step(ft, 4, ha, hb, spa, spb, av[0], bv[0]);
+        }
 #pragma unroll
         for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
         if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, (part % 4) % TA, part % 4);
-        if (t == 0) interleave(std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
-        if (t == 1) interleave(std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
-        if (t == 2) interleave(std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
-        if (t == 3) interleave(std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
+        if constexpr (F > 0) {
+          if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
+          if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
+          if (t == 2) interleave(ft, std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
+          if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
+        }
       }
       // step g + 1 has landed: at most the transfers issued since the
       // fetch of step g + 1 (the last AHEAD - 1 steps' codes, and scales) remain
@@ -894,28 +922,32 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       // the next step's first half (at a tile's last step: not used)
       const uint32_t nks = ks + 1 < nsteps ? ks + 1 : 0;
       uint32_t na[FM], nb[FN];
-      read_half(g + 1, 0, fa, fb);
-      read_scales(ti * cpt + nks / SC_STEPS, nks, na, nb);
+      if constexpr (F > 0) {
+        read_half(ft, g + 1, 0, fa, fb);
+        read_scales(ft, ti * cpt + nks / SC_STEPS, nks, na, nb);
+      }
       __builtin_amdgcn_sched_barrier(0);
       half2v npa[FM][2], npb[FN][2];
+      if constexpr (F > 0) {
 #pragma unroll
-      for (int t = 4; t < 8; ++t) {
-        mfmas(av[t & 1], bv[t & 1]);
-        if (t < 7) {
-          decode_step(t + 1, ha, hb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
-        } else {
-          // keep the next step's operands from being used (and waited for) earlier
+        for (int t = 4; t < 8; ++t) {
+          mfmas(ft, av[t & 1], bv[t & 1]);
+          if (t < 7) {
+            decode_step(ft, t + 1, ha, hb, spa, spb, av[(t + 1) & 1], bv[(t + 1) & 1]);
+          } else {
+            // keep the next step's operands from being used (and waited for) earlier
 #pragma unroll
-          for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
+            for (int i = 0; i < F; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
 #pragma unroll
-          for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
-          pairs(na, nb, npa, npb);
-          decode_step(0, fa, fb, npa, npb, av[0], bv[0]);
+            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
+            pairs(ft, na, nb, npa, npb);
+            decode_step(ft, 0, fa, fb, npa, npb, av[0], bv[0]);
+          }
+          interleave(ft, std::integral_constant<int, 0>());
         }
-        interleave(std::integral_constant<int, 0>());
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < F; ++i) {
         spa[i][0] = npa[i][0];
         spa[i][1] = npa[i][1];
       }
@@ -925,9 +957,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         spb[j][1] = npb[j][1];
       }
     }
+    };
+    // dispatch on F (uniform per wave; every variant runs the same barriers)
+    if (nf >= (uint32_t)FM) run(std::integral_constant<int, FM>());
+    else if (nf == 0) run(std::integral_constant<int, 0>());
+    else if (nf == 1) run(std::integral_constant<int, 1>());
+    else if constexpr (FM > 2) {
+      if (nf == 2) run(std::integral_constant<int, 2>());
+      else if constexpr (FM > 3) run(std::integral_constant<int, 3>());
+    }
+
     // the tile is done: the next tile's first steps are already in flight
     wait_lgkm0();
-    epilogue(g - 1, row0, tile_n);
+    epilogue(g - 1, row0, tile_n, nf);
     __syncthreads();  // staging done before the next step's transfers
 #pragma unroll
     for (int i = 0; i < FM; ++i)
