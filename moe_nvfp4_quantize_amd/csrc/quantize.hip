@@ -416,8 +416,9 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
 #pragma unroll
   for (int i = 0; i < U; ++i) {
     const uint32_t u = i * stride + blockIdx.x * NT + tid;
-    bmax[i] = u < p.units ? raw_max<T>(w[i]) : 0.0f;
-    m = fmaxf(m, bmax[i]);
+    const float b = u < p.units ? raw_max<T>(w[i]) : 0.0f;
+    if (MODE != kFp8) bmax[i] = b;  // FP8 needs only the tensor's max: no registers kept
+    m = fmaxf(m, b);
   }
   m = block_max(m);
 
@@ -517,8 +518,9 @@ hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, 
     if (u1024 <= 4) return launch_resident_u<T, VEC, 4, 1024, MODE>(p, st, G, stream);
     if (u1024 <= 6) return launch_resident_u<T, VEC, 6, 1024, MODE>(p, st, G, stream);
     if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, MODE>(p, st, G, stream);
-    // the decode-and-store of quantize-dequantize needs more than 128 VGPRs at 10
-    if (MODE != kQdq && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, MODE>(p, st, G, stream);
+    // at 10 blocks per thread the encodes of quantize-dequantize (decode and
+    // store) and of FP8 (sixteen converts per block) need more than 128 VGPRs
+    if (MODE == kNvfp4 && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, MODE>(p, st, G, stream);
     if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, MODE>(p, st, G, stream);
     if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, MODE>(p, st, G, stream);
   } else {
