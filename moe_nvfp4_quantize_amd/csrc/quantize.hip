@@ -520,7 +520,8 @@ hipError_t launch_resident(const QuantParams &p, ResidentState *st, uint32_t G, 
     if (u1024 <= 8) return launch_resident_u<T, VEC, 8, 1024, MODE>(p, st, G, stream);
     // at 10 blocks per thread the encodes of quantize-dequantize (decode and
     // store) and of FP8 (sixteen converts per block) need more than 128 VGPRs
-    if (MODE == kNvfp4 && u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, MODE>(p, st, G, stream);
+    if constexpr (MODE == kNvfp4)
+      if (u1024 <= 10) return launch_resident_u<T, VEC, 10, 1024, MODE>(p, st, G, stream);
     if (u512 <= 16) return launch_resident_u<T, VEC, 16, 512, MODE>(p, st, G, stream);
     if (u512 <= 20) return launch_resident_u<T, VEC, 20, 512, MODE>(p, st, G, stream);
   } else {
