@@ -451,25 +451,52 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   const uint32_t nsteps = K / 128, cpt = (nsteps + SC_STEPS - 1) / SC_STEPS;
 
   // ---------------------------------------------------------------- tiles
-  // Dense: workgroup b computes tiles b, b + G, b + 2G, ... (G = gridDim.x, a
-  // multiple of 8, so they all map to the XCD of b; the host launches more
-  // than one tile per workgroup only when K % 1024 == 0).  Grouped: one tile.
+  // Dense: workgroup b computes work items b, b + G, b + 2G, ... (G =
+  // gridDim.x; when it exceeds one item per workgroup it is a multiple of 8,
+  // so they all map to the XCD of b; the host launches more than one item per
+  // workgroup only when K % 1024 == 0).  An item is a whole tile, except when
+  // the tiles left for the last round fill at most half of it: each of those
+  // is then split into its two halves of BM / 2 rows, which run on two
+  // workgroups of the same XCD (w and w + 8), so that round takes about half
+  // as long.  Grouped: one tile.
   uint32_t my_tiles, row0, row_end, tile_n;
   const uint8_t *bq = p.b_q, *bs = p.b_s;
   float b_g;
-  uint32_t tiles_m = 0;
-  auto origin = [&](uint32_t i, uint32_t *r0, uint32_t *tn) {
+  uint32_t tiles_m = 0, full = 0, rem = 0;
+  bool split = false;
+  auto origin = [&](uint32_t i, uint32_t *r0, uint32_t *re, uint32_t *tn) {
     uint32_t tm;
-    dense_tile(blockIdx.x + i * gridDim.x, tiles_m, tiles_n, &tm, tn);
-    *r0 = tm * BM;
+    const uint32_t w = blockIdx.x + i * gridDim.x;
+    if (split && w >= full * gridDim.x) {
+      // half j of the last round: halves of tile k on workgroups of one XCD
+      const uint32_t j = w - full * gridDim.x, nb = (2 * rem) / 16;
+      uint32_t k, half;
+      if (j < nb * 16) {
+        k = (j / 16) * 8 + j % 8;
+        half = (j / 8) % 2;
+      } else {
+        k = nb * 8 + (j - nb * 16) / 2;
+        half = (j - nb * 16) % 2;
+      }
+      dense_tile(full * gridDim.x + k, tiles_m, tiles_n, &tm, tn);
+      *r0 = tm * BM + half * (BM / 2);
+      *re = min(*r0 + BM / 2, p.M);
+    } else {
+      dense_tile(w, tiles_m, tiles_n, &tm, tn);
+      *r0 = tm * BM;
+      *re = p.M;
+    }
   };
   if (!GROUPED) {
     tiles_m = (p.M + BM - 1) / BM;
     const uint32_t ntiles = tiles_m * tiles_n;
-    if (blockIdx.x >= ntiles) return;
-    my_tiles = (ntiles - 1 - blockIdx.x) / gridDim.x + 1;
-    origin(0, &row0, &tile_n);
-    row_end = p.M;
+    full = ntiles / gridDim.x;
+    rem = ntiles % gridDim.x;
+    split = rem != 0 && 2 * rem <= gridDim.x && p.M > BM / 2;
+    const uint32_t items = split ? full * gridDim.x + 2 * rem : ntiles;
+    if (blockIdx.x >= items) return;
+    my_tiles = (items - 1 - blockIdx.x) / gridDim.x + 1;
+    origin(0, &row0, &row_end, &tile_n);
     b_g = *p.b_g;
   } else {
     // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM)
@@ -828,8 +855,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // rewriting identical bytes), so at the mid-step barrier one wait count
   // leaves in flight only what was issued after the fetch of the next step.  At the last step of a
   // tile its epilogue runs, behind the already issued transfers of the next.
-  uint32_t nrow0 = row0, ntile_n = tile_n;  // the tile after the current one
-  if (my_tiles > 1) origin(1, &nrow0, &ntile_n);
+  uint32_t nrow0 = row0, nrow_end = row_end, ntile_n = tile_n;  // the tile after the current one
+  if (my_tiles > 1) origin(1, &nrow0, &nrow_end, &ntile_n);
 #pragma unroll
   for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j % TA, j);
   // steps 0 .. AHEAD - 1 (a short single tile reloads its last step into the
@@ -978,8 +1005,9 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     row0 = nrow0;
+    row_end = nrow_end;
     tile_n = ntile_n;
-    if (ti + 2 < my_tiles) origin(ti + 2, &nrow0, &ntile_n);
+    if (ti + 2 < my_tiles) origin(ti + 2, &nrow0, &nrow_end, &ntile_n);
   }
 }
 
@@ -1018,10 +1046,13 @@ bool dma_ok(const GemmParams &p, uint64_t a_rows) {
 // workgroup per compute unit, each walking its tiles with the next tile's
 // first K steps fetched during the current tile's last ones; otherwise one
 // workgroup per tile.  The CU count is a multiple of 8, which keeps every
-// workgroup's tiles on one XCD.
-uint32_t persistent_grid(const GemmParams &p, uint32_t tiles) {
-  if ((p.K / 128) % 8 != 0) return tiles;
+// workgroup's tiles on one XCD.  A product with at most half as many tiles as
+// compute units launches two workgroups per tile, one per half of its rows
+// (the kernel splits the tiles of a last round that is at most half full).
+uint32_t dense_grid(const GemmParams &p, uint32_t tiles, uint32_t bm) {
   const uint32_t g = device_cu_count() & ~7u;
+  if (g != 0 && 2 * tiles <= g && p.M > bm / 2) return 2 * tiles;
+  if ((p.K / 128) % 8 != 0) return tiles;
   return g == 0 || tiles <= g ? tiles : g;
 }
 
@@ -1088,7 +1119,7 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
     auto go = [&](auto bm_tag) -> hipError_t {
       constexpr int TBM = decltype(bm_tag)::value;
       const uint32_t tiles = ((p.N + BN - 1) / BN) * ((p.M + TBM - 1) / TBM);
-      const uint32_t g = persistent_grid(p, tiles);
+      const uint32_t g = dense_grid(p, tiles, TBM);
       if (out == OutType::BF16)
         return vs ? launch_dma<TBM, false, false, true, uint16_t>(p, g, stream)
                   : launch_dma<TBM, false, false, false, uint16_t>(p, g, stream);

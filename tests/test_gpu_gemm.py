@@ -125,6 +125,32 @@ def test_ragged_shapes(B, M, N, K, out_dtype):
     _compare(y, G.gemm(*a, *b), out_dtype, f"ragged {M}x{N}x{K}")
 
 
+def _random_nvfp4(rng, rows, K, g):
+    """Operands straight in the format: any code byte, block scales from 0.25
+    to 15 (E4M3 codes 0x28 .. 0x57)."""
+    return (rng.integers(0, 256, (rows, K // 2), dtype=np.uint8),
+            rng.integers(0x28, 0x58, (rows, K // 16), dtype=np.uint8), np.float32(g))
+
+
+# Tile walks on a 256-CU device (tiles of 128 rows for M <= 128, else 256; 256
+# columns): a last round at most half full runs each of its tiles as two
+# halves of rows, and a product of at most 128 tiles runs every tile that way.
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    (1000, 17000, 1024, torch.float32),   # 268 tiles: 12 split, ragged last rows 768..999
+    (100, 70000, 1024, torch.bfloat16),   # 274 tiles of 128 rows: 18 split, halves of 64 and 36 rows
+    (100, 3000, 1024, torch.float32),     # 12 tiles, all split
+    (65, 1000, 1024, torch.float32),      # second halves hold one row
+    (129, 700, 256, torch.bfloat16),      # 256-row tiles, K with no persistent walk
+    (300, 5000, 2048, torch.float32),     # 40 tiles in two tile rows, all split
+    (250, 36000, 1024, torch.float32),    # 141 tiles: one each, none split
+])
+def test_split_tile_walks_full_output(B, M, N, K, out_dtype):
+    rng = np.random.default_rng(M + N + K)
+    a, b = _random_nvfp4(rng, M, K, 2.0 ** -4), _random_nvfp4(rng, N, K, 2.0 ** -6)
+    y = _run(B, a, b, out_dtype)
+    _compare(y, G.gemm(*a, *b), out_dtype, f"walk {M}x{N}x{K}")
+
+
 def test_output_row_stride(B):
     rng = np.random.default_rng(1)
     a = Q.quantize(rng.standard_normal((20, 64)).astype(np.float32))
