@@ -499,10 +499,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     origin(0, &row0, &row_end, &tile_n);
     b_g = *p.b_g;
   } else {
-    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM)
+    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM).
+    // Workgroup b runs on XCD b % 8: XCD x takes M tiles x, x + 8, x + 16, ...,
+    // each with all its N tiles in a row, so that the gathered rows of an M tile
+    // are fetched into one L2, and the M tiles past the last real one (the grid
+    // covers an upper bound, a multiple of 8 M tiles) leave every XCD alike.
     my_tiles = 1;
-    tile_n = blockIdx.x % tiles_n;
-    const uint32_t tile_mm = blockIdx.x / tiles_n;
+    const uint32_t wl = blockIdx.x / 8;
+    tile_n = wl % tiles_n;
+    const uint32_t tile_mm = 8 * (wl / tiles_n) + blockIdx.x % 8;
     if (tid == 0) sInfo[0] = -1;
     uint32_t base = 0;
     for (uint32_t c0 = 0; c0 < p.E; c0 += 256) {
@@ -1150,7 +1155,9 @@ hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epi
   if (qout && !(al && dma_ok(p, p.a_rows))) return hipErrorNotSupported;
   if (al && dma_ok(p, p.a_rows)) {
     const int bm = grouped_tile_rows(R, p.E);
-    const uint32_t grid = grid_for((uint32_t)bm);
+    // M tiles rounded up to a multiple of 8 (the kernel's XCD-major tile order)
+    const uint64_t mt = ((uint64_t)R + bm - 1) / bm + p.E;
+    const uint32_t grid = (uint32_t)(((mt + 7) & ~(uint64_t)7) * tiles_n);
     auto go = [&](auto bm_tag) -> hipError_t {
       constexpr int TBM = decltype(bm_tag)::value;
       if (qout) return launch_dma<TBM, true, true, false, float, true>(p, grid, stream);
