@@ -367,8 +367,14 @@ def report_moe(st, timer, step_ms):
     gu_tflops = f_gu / (gu_ms * 1e-3) / 1e12
     kernel = "nvfp4 gemm_dma_kernel" if H % 256 == 0 else "nvfp4 gemm_kernel"
     kernel += " (grouped, SiLU gate" + (" -> NVFP4 h)" if st["static"] else ")")
+    # HBM bytes of the gate_up launch from the committed summary of the dynamic
+    # step (the static step's gate_up writes NVFP4 h instead: not measured)
+    traffic = None
+    if not st["static"]:
+        traffic = profiled_traffic(f"moe_step_{st['name'][len('moe_'):]}.md",
+                                   "moe_nvfp4_quantize_amd/csrc/gemm.hip")
     roof = dict(bound="mfma", achieved=gu_tflops, peak=F16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel=kernel, traffic=None,
+                frac=gu_tflops / F16_MFMA_PEAK_TFLOPS, kernel=kernel, traffic=traffic,
                 per_launch=dict(flops=f_gu, avg_ms=gu_ms))
     parts = {n: timer.mean_ms(n) for n in timer.names}
     d_ms = parts["down"]
