@@ -509,31 +509,36 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     tile_n = wl % tiles_n;
     const uint32_t tile_mm = 8 * (wl / tiles_n) + blockIdx.x % 8;
     if (tid == 0) sInfo[0] = -1;
-    uint32_t base = 0;
-    for (uint32_t c0 = 0; c0 < p.E; c0 += 256) {
-      const uint32_t e = c0 + tid;
-      uint32_t cnt = 0, lo = 0;
-      if (e < p.E) {
-        lo = (uint32_t)p.expert_offsets[e];
-        cnt = ((uint32_t)p.expert_offsets[e + 1] - lo + BM - 1) / BM;
-      }
-      scan[tid] = cnt;
-      __syncthreads();
-      for (uint32_t off = 1; off < 256; off <<= 1) {
-        const uint32_t v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-      }
-      const uint32_t incl = base + scan[tid];
-      const uint32_t excl = incl - cnt;
-      if (e < p.E && cnt && tile_mm >= excl && tile_mm < incl) {
-        sInfo[0] = (int32_t)e;
-        sInfo[1] = (int32_t)(lo + (tile_mm - excl) * BM);
-      }
-      base += scan[255];
-      __syncthreads();
+    // Exclusive prefix over experts of ceil(n_e / BM) in one pass: thread t owns
+    // experts [t * per, t * per + per); a scan of the threads' sums inside each
+    // wave, then the four waves' totals through LDS.
+    const uint32_t per = (p.E + 255) / 256, e_lo = tid * per, e_hi = min(e_lo + per, p.E);
+    uint32_t own = 0;
+    for (uint32_t e = e_lo; e < e_hi; ++e)
+      own += ((uint32_t)p.expert_offsets[e + 1] - (uint32_t)p.expert_offsets[e] + BM - 1) / BM;
+    uint32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off, 64);
+      if (lane >= (uint32_t)off) incl += v;
     }
+    if (lane == 63) scan[wave] = incl;
+    __syncthreads();
+    uint32_t first = incl - own;  // M tiles before this thread's first expert
+    for (uint32_t w = 0; w < wave; ++w) first += scan[w];
+    if (tile_mm >= first && tile_mm < first + own) {
+      for (uint32_t e = e_lo; e < e_hi; ++e) {
+        const uint32_t lo = (uint32_t)p.expert_offsets[e];
+        const uint32_t cnt = ((uint32_t)p.expert_offsets[e + 1] - lo + BM - 1) / BM;
+        if (tile_mm < first + cnt) {
+          sInfo[0] = (int32_t)e;
+          sInfo[1] = (int32_t)(lo + (tile_mm - first) * BM);
+          break;
+        }
+        first += cnt;
+      }
+    }
+    __syncthreads();
     if (sInfo[0] < 0) return;  // past the last tile: the whole workgroup leaves
     const uint32_t e = (uint32_t)sInfo[0];
     row0 = (uint32_t)sInfo[1];
