@@ -45,29 +45,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     const uint32_t e = lane + 64u * i;
     v[i] = e < E ? row[e] : -INFINITY;
   }
-  uint32_t taken = 0;  // bit i: expert lane + 64 i already selected
+  // bit i: expert lane + 64 i is selectable (exists, not yet selected)
+  uint32_t open = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) open |= (lane + 64u * i < E ? 1u : 0u) << i;
   float sel_v = 0.0f;  // lane j < k keeps the j-th selection
   int32_t sel_e = 0;
   for (uint32_t j = 0; j < k; ++j) {
+    // candidates compared without branches: larger value first, then lower id
     float bv = -INFINITY;
     int32_t be = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-      const uint32_t e = lane + 64u * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && (int32_t)e < be))) {
-        bv = v[i];
-        be = (int32_t)e;
-      }
+      const int32_t e = (int32_t)(lane + 64u * i);
+      const bool take = ((open >> i) & 1u) & ((v[i] > bv) | ((v[i] == bv) & (e < be)));
+      bv = take ? v[i] : bv;
+      be = take ? e : be;
     }
+#pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const float ov = __shfl_xor(bv, off, 64);
       const int32_t oe = __shfl_xor(be, off, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
+      const bool take = (ov > bv) | ((ov == bv) & (oe < be));
+      bv = take ? ov : bv;
+      be = take ? oe : be;
     }
-    if ((uint32_t)be % 64u == lane) taken |= 1u << ((uint32_t)be / 64u);
+    if ((uint32_t)be % 64u == lane) open &= ~(1u << ((uint32_t)be / 64u));
     if (lane == j) {
       sel_v = bv;
       sel_e = be;
@@ -111,11 +114,22 @@ __global__ __launch_bounds__(64) void count_kernel(const int32_t *ids, uint32_t 
 // of group g's first token with expert e is offsets[e] + counts[g][e].
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t *counts, uint32_t G, uint32_t E,
                                                     int32_t *offsets) {
-  __shared__ int32_t part[1024];
-  const uint32_t e = threadIdx.x;
+  __shared__ int32_t part[16];
+  const uint32_t e = threadIdx.x, lane = e % 64, wv = e / 64;
   int32_t run = 0;
   if (e < E) {
     uint32_t g = 0;
+    // 32 loads in flight per thread: the column walk is a chain of memory latencies
+    for (; g + 32 <= G; g += 32) {
+      int32_t c[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) c[i] = counts[(int64_t)(g + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        counts[(int64_t)(g + i) * E + e] = run;
+        run += c[i];
+      }
+    }
     for (; g + 8 <= G; g += 8) {
       int32_t c[8];
 #pragma unroll
@@ -132,16 +146,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *counts, uint32_t G,
       run += c;
     }
   }
-  part[e] = run;
-  __syncthreads();
-  for (uint32_t off = 1; off < 1024; off <<= 1) {
-    const int32_t v = e >= off ? part[e - off] : 0;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
+  // exclusive scan of the column totals over e: inside each wave, then the
+  // sixteen wave totals through LDS (threads e >= E contribute 0)
+  int32_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(incl, off, 64);
+    if (lane >= (uint32_t)off) incl += v;
   }
-  if (e < E) offsets[e] = part[e] - run;
-  if (e == 1023) offsets[E] = part[1023];
+  if (lane == 63) part[wv] = incl;
+  __syncthreads();
+  int32_t before = 0;
+  for (uint32_t w = 0; w < wv; ++w) before += part[w];
+  if (e < E) offsets[e] = before + incl - run;
+  if (e == 1023) offsets[E] = before + incl;
 }
 
 __global__ __launch_bounds__(64) void place_kernel(const int32_t *ids, uint32_t T, uint32_t E,
