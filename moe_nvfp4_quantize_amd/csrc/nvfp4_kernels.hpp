@@ -20,7 +20,10 @@ struct ResidentState {
   uint32_t parity;     // which slot array the current launch uses
   uint32_t done;       // workgroups finished in the current launch
   uint32_t fallbacks;  // workgroups whose wait expired (diagnostic; 0 when co-resident)
-  uint32_t pad;
+  // bound on each arrival wait, in polls; 0 (the zero-filled state) means the
+  // built-in bound.  The kernels never write it: a caller may set a tiny bound
+  // to force the expired-wait path (a test of that path).
+  uint32_t spin_limit;
   // slot[p][w] = 0x80000000 | bits(max|x| of workgroup w): arrival flag and
   // value in one word, written and read with relaxed atomics
   uint32_t slot[2][kMaxResidentWGs];

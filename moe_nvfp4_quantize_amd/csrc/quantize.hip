@@ -429,13 +429,15 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
                        __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  const uint32_t lim0 = __hip_atomic_load(&st->spin_limit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t lim = lim0 ? lim0 : kSpinLimit;
   float a = 0.0f;
   for (uint32_t i = tid; i < G; i += NT) {
     uint32_t v = 0;
     for (uint32_t spin = 0;; ++spin) {
       v = __hip_atomic_load(&st->slot[par][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v & 0x80000000u) break;
-      if (spin >= kSpinLimit) {
+      if (spin >= lim) {
         s_fallback = 1u;
         break;
       }

@@ -229,3 +229,35 @@ def test_many_calls_reuse_the_workspace(B):
         np.testing.assert_array_equal(s[rr].cpu().numpy(), rs)
         np.testing.assert_array_equal(q[rr].cpu().numpy(), rq)
     assert _barrier_timeouts(B) == before == 0
+
+
+def test_expired_waits_take_the_whole_tensor_max(B):
+    """The single-read kernel's bounded arrival wait, forced to expire from the
+    host: word 3 of the workspace's arrival state holds a wait bound in polls (0:
+    the built-in bound) that the kernels never write.  At one poll most
+    workgroups stop waiting and read the whole tensor for the max themselves;
+    codes, scales and the global scale stay bit-exact, the expired waits are
+    counted (word 2), and a call with the built-in bound then runs on the same
+    workspace.  Called through the C-ABI with a workspace of the test's own."""
+    lib = B.load_library()
+    rows, cols = 1024, 2048
+    ws = torch.zeros(int(lib.nvfp4_quantize_workspace_size(rows, cols)), dtype=torch.uint8, device="cuda")
+    words = ws[:16].view(torch.int32)
+    for i, bound in enumerate([1, 1, 0]):
+        print(f"[quantize] wait bound {bound}, call {i}", flush=True)
+        x = W.random_matrix(rows, cols, seed=300 + i, dtype=torch.bfloat16, device="cuda") * (1.0 + i)
+        words[3] = bound
+        words[2] = 0
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda")
+        g = torch.empty(1, dtype=torch.float32, device="cuda")
+        st = lib.nvfp4_quantize(B._ptr(x), B.NVFP4_BF16, rows, cols, cols, B._ptr(q), B._ptr(s), B._ptr(g), 0,
+                                B._ptr(ws), ws.numel(), B._stream())
+        assert st == 0
+        torch.cuda.synchronize()
+        rq, rs, rg = Q.quantize(_host(x))
+        assert g.item() == rg, i
+        np.testing.assert_array_equal(s.cpu().numpy(), rs)
+        np.testing.assert_array_equal(q.cpu().numpy(), rq)
+        if bound:
+            assert int(words[2].item()) > 0, "no wait expired at a bound of one poll"
