@@ -393,7 +393,7 @@ __device__ float whole_tensor_max(const QuantParams &p) {
 template <typename T, bool VEC, int U, int NT, int MODE>
 __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentState *st) {
   __shared__ float rtab[128];
-  __shared__ uint32_t s_fallback;
+  __shared__ uint32_t s_fallback, s_lim;
   const uint32_t tid = threadIdx.x, G = gridDim.x;
   const uint32_t stride = G * NT;
   const T *x = static_cast<const T *>(p.x);
@@ -425,12 +425,15 @@ __global__ __launch_bounds__(NT) void resident_kernel(QuantParams p, ResidentSta
   // publish, then gather every workgroup's max
   if (tid == 0) {
     s_fallback = 0u;
+    const uint32_t l = __hip_atomic_load(&st->spin_limit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_lim = l ? l : kSpinLimit;
     __hip_atomic_store(&st->slot[par][blockIdx.x], 0x80000000u | f2u(m), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  const uint32_t lim0 = __hip_atomic_load(&st->spin_limit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t lim = lim0 ? lim0 : kSpinLimit;
+  // the wait bound, read once per workgroup (an agent-scope load of one word by
+  // every thread cost a single-read quantize-dequantize pass 30% of its time)
+  const uint32_t lim = s_lim;
   float a = 0.0f;
   for (uint32_t i = tid; i < G; i += NT) {
     uint32_t v = 0;
