@@ -161,6 +161,18 @@ def test_grouped_gemm_small(B, T, E, k, H, N, epi):
     _grouped_case(B, T, E, k, H, N, epi, seed=T + E + N)
 
 
+# K of 1024 or 2048 and an even number of 256-column N tiles: without the SiLU
+# gate and with 128- and 192-row tiles each workgroup computes two N tiles of one
+# M tile in a row (the second one's first K steps fetched during the first one's
+# last); the gated and the 256-row cases beside them keep one N tile each.
+# Every expert is checked.
+@pytest.mark.parametrize("T,E,k,H,N,epi", [(500, 16, 4, 1024, 512, 1), (600, 4, 1, 1024, 512, 0),
+                                           (200, 7, 2, 2048, 1024, 1), (200, 7, 2, 2048, 1024, 0),
+                                           (300, 6, 2, 1024, 2048, 0), (1000, 8, 2, 1024, 512, 1)])
+def test_grouped_gemm_two_tile_walk(B, T, E, k, H, N, epi):
+    _grouped_case(B, T, E, k, H, N, epi, seed=T + E + N + epi)
+
+
 def test_grouped_gemm_without_gather(B):
     _grouped_case(B, 300, 6, 2, 256, 128, 0, seed=3, gather=False)
 
@@ -182,7 +194,8 @@ def test_grouped_gemm_full_shapes_sampled(B, name, stage):
 
 
 @pytest.mark.parametrize("T,E,k,H,I,g_div", [(200, 7, 2, 256, 128, 1.0), (500, 16, 4, 512, 192, 1.0),
-                                             (600, 4, 1, 512, 128, 8.0), (2000, 2, 1, 256, 256, 1.0)])
+                                             (600, 4, 1, 512, 128, 8.0), (2000, 2, 1, 256, 256, 1.0),
+                                             (500, 16, 4, 1024, 256, 1.0), (300, 6, 2, 2048, 512, 1.0)])
 def test_gate_up_nvfp4_epilogue(B, T, E, k, H, I, g_div):
     """The fused epilogue's h bytes equal the oracle's static quantization of the
     unfused kernel's float32 h (same accumulation, so the same h), bit for bit.
