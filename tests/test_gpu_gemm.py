@@ -151,6 +151,21 @@ def test_split_tile_walks_full_output(B, M, N, K, out_dtype):
     _compare(y, G.gemm(*a, *b), out_dtype, f"walk {M}x{N}x{K}")
 
 
+# Seeded random shapes (K from 256 to 3072, M up to 700, N up to 40000) plus
+# persistent walks with whole rounds (K % 1024 == 0, more tiles than compute
+# units, with and without a split last round); full outputs against the oracle.
+@pytest.mark.parametrize("M,N,K", [(82, 14634, 256), (62, 7258, 1024), (26, 32132, 768), (344, 16484, 2048),
+                                   (92, 22309, 768), (423, 9234, 256), (154, 23826, 2048), (221, 38386, 1024),
+                                   (248, 33185, 1280), (123, 37718, 1280),
+                                   (700, 30000, 1024), (128, 80000, 1024), (513, 20000, 2048)])
+def test_random_shapes_full_output(B, M, N, K):
+    rng = np.random.default_rng(M * 131 + N + K)
+    a, b = _random_nvfp4(rng, M, K, 2.0 ** -5), _random_nvfp4(rng, N, K, 2.0 ** -7)
+    out_dtype = torch.bfloat16 if (M + N) % 2 else torch.float32
+    y = _run(B, a, b, out_dtype)
+    _compare(y, G.gemm(*a, *b), out_dtype, f"random {M}x{N}x{K}")
+
+
 def test_output_row_stride(B):
     rng = np.random.default_rng(1)
     a = Q.quantize(rng.standard_normal((20, 64)).astype(np.float32))
