@@ -261,3 +261,39 @@ def test_expired_waits_take_the_whole_tensor_max(B):
         np.testing.assert_array_equal(q.cpu().numpy(), rq)
         if bound:
             assert int(words[2].item()) > 0, "no wait expired at a bound of one poll"
+
+
+def test_concurrent_streams_stay_exact(B):
+    """Dynamic quantizes of two tensors issued on two streams at once (default
+    priority, one cached workspace each): the single-read kernels share the
+    compute units, so a workgroup may wait past its bound and read the whole
+    tensor for the max; codes, scales and global scales stay exact either way."""
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    xs = [W.random_matrix(4096, 5120, seed=400 + i, dtype=torch.bfloat16, device="cuda") * (1.0 + 3 * i)
+          for i in range(2)]
+    torch.cuda.synchronize()
+    outs = []
+    for it in range(3):
+        print(f"[quantize] two streams, round {it}", flush=True)
+        with torch.cuda.stream(s1):
+            r1 = B.nvfp4_quantize(xs[0])
+        with torch.cuda.stream(s2):
+            r2 = B.nvfp4_quantize(xs[1])
+        outs.append((r1, r2))
+    torch.cuda.synchronize()
+    keys = [k for k in B._QWS if k[1] in (s1.cuda_stream, s2.cuda_stream)]
+    waits = sum(int(B._QWS[k][8:12].view(torch.int32).item()) for k in keys)
+    print(f"[quantize] two streams: {waits} expired waits", flush=True)
+    for x, i in zip(xs, range(2)):
+        xh = _host(x)
+        rg = Q.global_scale(xh)
+        rows = np.array([0, 1, 4095] + list(range(7, 4096, 331)))
+        rq, rs, _ = Q.quantize(xh[rows], g=rg)
+        for pair in outs:
+            q, s, g = pair[i]
+            assert g.item() == rg
+            sel = torch.as_tensor(rows, device="cuda")
+            np.testing.assert_array_equal(s[sel].cpu().numpy(), rs)
+            np.testing.assert_array_equal(q[sel].cpu().numpy(), rq)
+    for k in keys:  # these workspaces were only for this test
+        del B._QWS[k]
