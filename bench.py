@@ -46,7 +46,9 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # the first ~20 GEMM launches of a process run slower (2.05 ms falling to a
+    # steady 1.61 ms for the prefill GEMM) while the clock settles
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="prefill_8192x5120", choices=sorted(W.WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--static-scales", action="store_true",
