@@ -108,6 +108,14 @@ class Timer:
         pairs = self.ev[name]
         return sum(a.elapsed_time(b) for a, b in pairs) / max(1, len(pairs))
 
+    def spread_ms(self, name):
+        """p10 / median / p90 of the per-step durations (nearest rank)."""
+        v = sorted(a.elapsed_time(b) for a, b in self.ev[name])
+        if not v:
+            return {}
+        pick = lambda q: v[min(len(v) - 1, int(q * len(v)))]
+        return dict(p10_ms=pick(0.1), median_ms=pick(0.5), p90_ms=pick(0.9))
+
 
 # ----------------------------------------------------------------- dense
 
@@ -234,9 +242,10 @@ def report_dense(st, timer, step_ms):
     q_gbs = qbytes / (q_ms * 1e-3) / 1e9
     extra = dict(
         gemm=dict(avg_ms=gemm_ms, tflops=gemm_tflops, frac_f16_peak=gemm_tflops / F16_MFMA_PEAK_TFLOPS,
-                  frac_fp4_peak=gemm_tflops / FP4_MFMA_PEAK_TFLOPS, gbs=gemm_gbs),
+                  frac_fp4_peak=gemm_tflops / FP4_MFMA_PEAK_TFLOPS, gbs=gemm_gbs, **timer.spread_ms("gemm")),
         quantize=dict(avg_ms=q_ms, gbs=q_gbs, frac_hbm=q_gbs / HBM_PEAK_GBS,
-                      algorithmic_bytes=qbytes, note="in-step interval, after the GEMM"),
+                      algorithmic_bytes=qbytes, note="in-step interval, after the GEMM",
+                      **timer.spread_ms("quantize")),
     )
     if "quantize_iso_ms" in st:
         iso = st["quantize_iso_ms"]
@@ -380,7 +389,8 @@ def report_moe(st, timer, step_ms):
                 per_launch=dict(flops=f_gu, avg_ms=gu_ms))
     parts = {n: timer.mean_ms(n) for n in timer.names}
     d_ms = parts["down"]
-    extra = dict(stages_ms=parts, down=dict(tflops=f_d / (d_ms * 1e-3) / 1e12))
+    extra = dict(stages_ms=parts, stages_spread_ms={n: timer.spread_ms(n) for n in timer.names},
+                 down=dict(tflops=f_d / (d_ms * 1e-3) / 1e12))
     if "quantize_h" in parts:
         qh_bytes = quant_bytes(R * I, 2)  # h stored in bf16
         extra["quantize_h"] = dict(gbs=qh_bytes / (parts["quantize_h"] * 1e-3) / 1e9)
