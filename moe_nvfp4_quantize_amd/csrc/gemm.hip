@@ -21,10 +21,10 @@
 //  * Packed operands stay packed until the last moment: global -> LDS moves
 //    0.5625 B per element (codes + scales), a quarter of an f16 GEMM's LDS
 //    traffic.  Two kernels share the decode and the epilogue: gemm_dma_kernel
-//    (dense, K % 256 == 0, aligned operands; described where it is defined)
-//    and gemm_kernel (grouped, ragged K, unaligned operands), whose loads go
-//    through registers into a double-buffered LDS stage while the current one
-//    is multiplied.
+//    (dense and grouped, K % 256 == 0, aligned operands; described where it is
+//    defined) and gemm_kernel (any valid K and alignment, dense and grouped),
+//    whose loads go through registers into a double-buffered LDS stage while
+//    the current one is multiplied.
 //  * Large wave tiles (up to 128 x 128 per wave) amortise each decoded
 //    fragment over 4 MFMAs in each direction: the decode work per MFMA falls as
 //    1/WM + 1/WN.
@@ -393,8 +393,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_kernel(Gem
 
 
 // ====================================================================
-// Dense kernel for K % 256 == 0 and aligned operands: global -> LDS without
-// registers, software-pipelined decode.
+// Main kernel (dense and grouped) for K % 256 == 0 and aligned operands:
+// global -> LDS without registers, software-pipelined decode.
 // ====================================================================
 
 // Grouped launches without the SiLU gate (down projections) and with short K
@@ -411,7 +411,8 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
          (n_out / bn_out) % 2 == 0;
 }
 
-// 256 x 256 output tile, four waves of 128 x 128 (4 x 4 MFMA tiles each).
+// BM x 256 output tile (BM = 128, 192 or 256), four waves of BM/2 x 128
+// (BM/64 x 4 MFMA tiles each).
 //  * Codes and scales go from global memory straight into LDS
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
 //    LDS), so no registers hold staged data and no LDS store instructions run.
@@ -420,17 +421,18 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
 //    tiles).  Scales: two chunks of eight K steps (64 bytes per
 //    row), so that a transfer reads 64 contiguous bytes of a row instead of 8;
 //    the next chunk is fetched during the first four steps of the current one.
-//  * Each step issues the same ten transfers (extra ones reload data that is
-//    not read any more, or rewrite identical bytes), so one wait count serves
+//  * Each step issues the same number of transfers (BM/64 + 4 code, 2 scale;
+//    extra ones reload data that is not read any more, or rewrite identical
+//    bytes), so one wait count serves
 //    every step: at the mid-step barrier only the step's own transfers may be
 //    in flight.  The transfers are spread over the step's MFMAs so that the
 //    memory pipeline never backs up the wave's in-order issue.
 //  * Fragments are double buffered in registers by half step (16-byte piece):
 //    the second half of step k is read at the start of step k, the first half
 //    of step k + 1 right after the mid-step barrier.
-//  * Decode is software pipelined: while the 16 MFMAs of sub-step t run, the
-//    operands of sub-step t + 1 are decoded (one MFMA, then four VALU
-//    instructions, sixteen times).
+//  * Decode is software pipelined: while the MFMAs of sub-step t run (16 for
+//    256-row tiles), the operands of sub-step t + 1 are decoded (one MFMA, then
+//    a few VALU instructions, in turn).
 template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   constexpr int BN = 256, WM = BM / 2, WN = 128, FM = WM / 32, FN = 4, HALF = FN / 2;
