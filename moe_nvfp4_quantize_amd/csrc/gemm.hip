@@ -88,7 +88,14 @@ __device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
   return (half8v){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z), with e^-z = 2^(-z log2 e) from the hardware base-2
+// exponential and the quotient from the hardware reciprocal (about 1 ulp each;
+// below z = -88.7 the power overflows to inf and the result is a signed zero).  The epilogue
+// evaluates one per output: the IEEE division and the range-reduced exp were
+// long dependent chains there.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
 
 template <typename OutT>
 __device__ __forceinline__ OutT to_out(float v);
