@@ -177,6 +177,49 @@ def test_grouped_gemm_without_gather(B):
     _grouped_case(B, 300, 6, 2, 256, 128, 0, seed=3, gather=False)
 
 
+@pytest.mark.parametrize("H,I", [(256, 128), (2048, 768)])
+def test_silu_gate_large_gate_values(B, H, I):
+    """Gate values of several hundred in magnitude: below z = -88.7 the power of
+    two in the kernel's SiLU overflows to inf, and h must come out as a signed
+    zero (the oracle's value is below 1e-30 there), never NaN; large positive
+    gates give h = gate * up.  Whole output within 1e-3 relative Frobenius error."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(H + I)
+    T, E, k = 300, 6, 2
+    r = B.nvfp4_moe_route(_routing(gen, T, E, k, dev, skew=True), k)
+    R = T * k
+    a_q, a_s, a_g = _rand_nvfp4(gen, (T, H), dev)
+    a = (a_q, a_s, a_g * 4096.0)  # GEMM outputs of a few hundred
+    w = _rand_nvfp4(gen, (E, 2 * I, H), dev)
+    out = B.nvfp4_moe_grouped_gemm(a, r["src_row"], r["offsets"], R, w,
+                                   epilogue=B.NVFP4_EPI_SILU_GATE, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    offsets = _np(r["offsets"]).astype(np.int64)
+    src = _np(r["src_row"])
+    got_all = _np(out)
+    assert np.isfinite(got_all[:R]).all()
+    n_neg = 0
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi == lo:
+            continue
+        rows = src[lo:hi]
+        gu = OG.gemm(a_q.cpu().numpy()[rows], a_s.cpu().numpy()[rows], np.float32(a[2][0].item()),
+                     _np(w[0][e]), _np(w[1][e]), np.float32(w[2][e].item()))
+        with np.errstate(over="ignore"):  # float64 e^-gate overflows below gate = -709: h = -0
+            ref = OM.silu_gate(gu)
+        got = got_all[lo:hi].astype(np.float64)
+        assert OG.rel_fro_error(got, ref) <= TOL, e
+        deep = gu[:, :I] < -100.0
+        n_neg += int(deep.sum())
+        assert (got[deep] == 0.0).all(), e
+    assert n_neg > 0, "no gate value below -100: the case does not reach the overflow"
+    big = np.abs(got_all[:R]).max()
+    print(f"[moe] SiLU gate H={H} I={I}: {n_neg} gates below -100 give h = 0, "
+          f"max |h| {big:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("name,stage", [("moe_e128_top8", "gate_up"), ("moe_e128_top8", "down"),
                                         ("moe_e512_top10", "gate_up"), ("moe_e512_top10", "down")])
 def test_grouped_gemm_full_shapes_sampled(B, name, stage):
