@@ -418,8 +418,9 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
          (n_out / bn_out) % 2 == 0;
 }
 
-// BM x 256 output tile (BM = 128, 192 or 256), four waves of BM/2 x 128
-// (BM/64 x 4 MFMA tiles each).
+// BM x 256 output tile (BM = 128, 192 or 256), four waves: 2 x 2 of BM/2 x 128
+// (BM/64 x 4 MFMA tiles each), or, for grouped 128- and 192-row tiles, 1 x 4
+// of BM x 64 (BM/32 x 2 MFMA tiles each).
 //  * Codes and scales go from global memory straight into LDS
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
 //    LDS), so no registers hold staged data and no LDS store instructions run.
@@ -440,10 +441,15 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
 //  * Decode is software pipelined: while the MFMAs of sub-step t run (16 for
 //    256-row tiles), the operands of sub-step t + 1 are decoded (one MFMA, then
 //    a few VALU instructions, in turn).
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
-  constexpr int BN = 256, WM = BM / 2, WN = 128, FM = WM / 32, FN = 4, HALF = FN / 2;
+  // NWM x NWN waves: 2 x 2 (waves of BM/2 x 128) or 1 x 4 (BM x 64)
+  constexpr int NWN = 4 / NWM;
+  constexpr int BN = 256, WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32, HALF = FN / 2;
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile height");
+  static_assert(NWM == 1 || NWM == 2, "wave grid");
+  static_assert(FM <= 8, "at most eight A fragments per wave");
+  static_assert(!QOUT || NWM == 2, "the NVFP4 epilogue quantizes 64-column wave slabs");
   static_assert(!SILU || GROUPED, "the SiLU epilogue is a grouped-GEMM epilogue");
   static_assert(!QOUT || (SILU && sizeof(OutT) == 4), "NVFP4 output: SiLU-gate epilogue, f32 staging");
   // transfers (64 lanes x 16 bytes) per operand: per code stage, and per scale chunk
@@ -687,17 +693,17 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
   };
 
-  const uint32_t wm = wave / 2, wn = wave % 2;
+  const uint32_t wm = wave / NWN, wn = wave % NWN;
   const uint32_t l32 = lane % 32, lh = lane / 32;
   // LDS byte offsets of this lane's fragment rows: codes (inside a stage) and
   // scales (inside a chunk, without the step's piece)
-  // A fragment i of wave half wm holds tile rows (2 i + wm) * 32 .. + 31: the
-  // 32-row groups alternate between the two halves, so that a tile whose
-  // rows end early leaves both halves about the same work
+  // A fragment i of wave row wm holds tile rows (NWM i + wm) * 32 .. + 31: with
+  // two wave rows the 32-row groups alternate between them, so that a tile
+  // whose rows end early leaves both about the same work
   uint32_t offA[FM][2], offB[FN][2], rowSA[FM], rowSB[FN], swA[FM], swB[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const uint32_t r = (2 * i + wm) * 32 + l32;
+    const uint32_t r = (NWM * i + wm) * 32 + l32;
 #pragma unroll
     for (int h = 0; h < 2; ++h) offA[i][h] = r * 64 + (((2 * lh + h) ^ swz(r)) * 16);
     rowSA[i] = r * 64 + lh * 4;
@@ -786,7 +792,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-      if (NV > 0 && k % (NM / (NV > 0 ? NV : 1)) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if constexpr (NV > 0 && NM >= NV) {
+        if (k % (NM / NV) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      } else if constexpr (NV > 0) {
+        // more transfers than MFMAs (a wave with one A fragment): spread evenly
+        const int nk = ((k + 1) * NV) / NM - (k * NV) / NM;
+#pragma unroll
+        for (int v = 0; v < nk; ++v) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -830,7 +843,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
-        const uint32_t rbase = r0 + (2 * i + wm) * 32 + ps * RPP;
+        const uint32_t rbase = r0 + (NWM * i + wm) * 32 + ps * RPP;
         if constexpr (QOUT) {
           // NVFP4 output with the static global scale: one 16-element block per
           // lane (RPP rows x ROW_ELEMS / 16 blocks), the quantizer's arithmetic
@@ -923,7 +936,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     // this wave's A fragments that hold rows of the tile
     const uint32_t rows_in = min(row_end - min(row0, row_end), (uint32_t)BM);
     const uint32_t groups = (rows_in + 31) / 32;
-    const uint32_t nf = groups > wm ? min((groups - wm + 1) / 2, (uint32_t)FM) : 0u;
+    const uint32_t nf = groups > wm ? min((groups - wm + NWM - 1) / NWM, (uint32_t)FM) : 0u;
     auto run = [&](auto f_tag) {
     constexpr int F = decltype(f_tag)::value;
     const auto ft = f_tag;
@@ -1041,7 +1054,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     else if (nf == 1) run(std::integral_constant<int, 1>());
     else if constexpr (FM > 2) {
       if (nf == 2) run(std::integral_constant<int, 2>());
-      else if constexpr (FM > 3) run(std::integral_constant<int, 3>());
+      else if constexpr (FM > 3) {
+        if (nf == 3) run(std::integral_constant<int, 3>());
+        else if constexpr (FM > 4) {
+          if (nf == 4) run(std::integral_constant<int, 4>());
+          else if constexpr (FM > 5) {
+            if (nf == 5) run(std::integral_constant<int, 5>());
+            else if constexpr (FM > 6) {
+              if (nf == 6) run(std::integral_constant<int, 6>());
+              else if constexpr (FM > 7) run(std::integral_constant<int, 7>());
+            }
+          }
+        }
+      }
     }
 
     // the tile is done: the next tile's first steps are already in flight
@@ -1106,19 +1131,20 @@ uint32_t dense_grid(const GemmParams &p, uint32_t tiles, uint32_t bm) {
   return g == 0 || tiles <= g ? tiles : g;
 }
 
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2>
 hipError_t launch_dma(const GemmParams &p, uint32_t grid, hipStream_t stream) {
-  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT, QOUT><<<grid, 256, 0, stream>>>(p);
+  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT, QOUT, NWM><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 // Tile height for the grouped GEMM from the mean rows per expert m = R / E.
 // Per-expert counts of a top-k router spread like a Poisson count around m,
 // and an expert with n rows costs ceil(n / BM) tiles of BM rows.  Shorter
-// tiles waste fewer rows but cost more per row: the wave tile is BM/2 x 128,
-// so the decode work per MFMA grows as BM shrinks, and a K step has fewer
-// MFMAs to hide it under.  Relative cost per computed row, measured on MI355X
-// with this kernel: 1.5 (128 rows), 1.2 (192), 1.0 (256).  The expected cost
+// tiles waste fewer rows but cost more per row: the decode work per MFMA
+// grows as BM shrinks, and a K step has fewer MFMAs to hide it under.
+// Relative cost per computed row, measured on MI355X with 2 x 2 waves: 1.5
+// (128 rows), 1.2 (192), 1.0 (256); the 1 x 4 waves that 128- and 192-row
+// tiles now use take 2-4% less time on the 512-expert workload's GEMMs.  The expected cost
 // of each height is estimated over 32 quantiles of a normal N(m, m) and the
 // cheapest height wins.
 int grouped_tile_rows(uint32_t R, uint32_t E) {
@@ -1207,18 +1233,24 @@ hipError_t launch_grouped_gemm(const GemmParams &p, uint32_t R, OutType out, Epi
     const uint32_t grid = (uint32_t)(((mt + 7) & ~(uint64_t)7) * tiles_n / tpw);
     auto go = [&](auto bm_tag) -> hipError_t {
       constexpr int TBM = decltype(bm_tag)::value;
+      // 128- and 192-row tiles: four waves side by side (1 x 4), each over all
+      // of the tile's rows, so a tile holding an odd number of 32-row groups
+      // keeps every wave busy (2 x 2 waves split 5 groups 3 + 2, the cost of
+      // 6); 256-row tiles stay 2 x 2, which leaves the registers for the
+      // pipeline (eight A fragments per wave would not fit)
+      constexpr int W = TBM == 256 ? 2 : 1;
       if (qout) return launch_dma<TBM, true, true, false, float, true>(p, grid, stream);
       if (silu)
         return out == OutType::BF16
-                   ? (vs ? launch_dma<TBM, true, true, true, uint16_t>(p, grid, stream)
-                         : launch_dma<TBM, true, true, false, uint16_t>(p, grid, stream))
-                   : (vs ? launch_dma<TBM, true, true, true, float>(p, grid, stream)
-                         : launch_dma<TBM, true, true, false, float>(p, grid, stream));
+                   ? (vs ? launch_dma<TBM, true, true, true, uint16_t, false, W>(p, grid, stream)
+                         : launch_dma<TBM, true, true, false, uint16_t, false, W>(p, grid, stream))
+                   : (vs ? launch_dma<TBM, true, true, true, float, false, W>(p, grid, stream)
+                         : launch_dma<TBM, true, true, false, float, false, W>(p, grid, stream));
       return out == OutType::BF16
-                 ? (vs ? launch_dma<TBM, true, false, true, uint16_t>(p, grid, stream)
-                       : launch_dma<TBM, true, false, false, uint16_t>(p, grid, stream))
-                 : (vs ? launch_dma<TBM, true, false, true, float>(p, grid, stream)
-                       : launch_dma<TBM, true, false, false, float>(p, grid, stream));
+                 ? (vs ? launch_dma<TBM, true, false, true, uint16_t, false, W>(p, grid, stream)
+                       : launch_dma<TBM, true, false, false, uint16_t, false, W>(p, grid, stream))
+                 : (vs ? launch_dma<TBM, true, false, true, float, false, W>(p, grid, stream)
+                       : launch_dma<TBM, true, false, false, float, false, W>(p, grid, stream));
     };
     if (bm == 256) return go(std::integral_constant<int, 256>());
     if (bm == 192) return go(std::integral_constant<int, 192>());
