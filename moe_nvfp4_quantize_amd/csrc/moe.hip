@@ -21,6 +21,7 @@
 #include "nvfp4_common.hpp"
 #include "nvfp4_format.hpp"
 #include "nvfp4_kernels.hpp"
+#include "moe_select.hpp"
 
 namespace nvfp4 {
 
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const uint32_t e = lane + 64u * i;
-    v[i] = e < E ? row[e] : -INFINITY;
+    v[i] = e < E ? router_logit(row[e]) : -INFINITY;
   }
   // bit i: expert lane + 64 i is selectable (exists, not yet selected)
   uint32_t open = 0;
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int32_t e = (int32_t)(lane + 64u * i);
-      const bool take = ((open >> i) & 1u) & ((v[i] > bv) | ((v[i] == bv) & (e < be)));
+      const bool take = ((open >> i) & 1u) & topk_before(v[i], e, bv, be);
       bv = take ? v[i] : bv;
       be = take ? e : be;
     }
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     for (int off = 32; off > 0; off >>= 1) {
       const float ov = __shfl_xor(bv, off, 64);
       const int32_t oe = __shfl_xor(be, off, 64);
-      const bool take = (ov > bv) | ((ov == bv) & (oe < be));
+      const bool take = topk_before(ov, oe, bv, be);
       bv = take ? ov : bv;
       be = take ? oe : be;
     }

@@ -12,6 +12,7 @@ s uint8 [rows, cols/16] (E4M3FN block scale codes) and g float32 [1] (the global
 decode scale), all on the GPU.
 """
 
+import atexit
 import ctypes
 import os
 
@@ -95,9 +96,12 @@ def _check(fn, status):
         raise NVFP4Error(fn, status)
 
 
+def _torch_stream(stream=None):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
 
 
 def _ptr(t):
@@ -123,17 +127,37 @@ def _ws(nbytes, device):
 
 
 # nvfp4_quantize's workspace must start zero-filled and then be reused: one per
-# (device, stream), grown (zero-filled again) when a larger one is needed.
+# (device, stream), grown (zero-filled again) when a larger one is needed.  It is
+# allocated and filled on the stream the kernels run on, so the fill is ordered
+# before them, and the caching allocator only hands a replaced buffer to later
+# work on that same stream, after the kernels that still read it.
 _QWS = {}
 
 
 def _quantize_ws(nbytes, device, stream):
-    key = (torch.device(device).index, int(stream.value or 0))
+    s = _torch_stream(stream)
+    key = (torch.device(device).index, int(s.cuda_stream))
     ws = _QWS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
         _QWS[key] = ws
     return ws
+
+
+@atexit.register
+def _release_workspaces():
+    """Drop the cached workspaces while the runtime is fully up: wait for the
+    kernels that use them, then release the tensors (before interpreter
+    teardown frees module state in no particular order)."""
+    if not _QWS:
+        return
+    try:
+        for dev in {k[0] for k in _QWS}:
+            torch.cuda.synchronize(dev)
+    except Exception:  # teardown: nothing left to protect
+        pass
+    _QWS.clear()
 
 
 # ------------------------------------------------------------------ quantize
@@ -161,7 +185,7 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
     if static and gg.data_ptr() != g.data_ptr():
         gg.copy_(g.reshape(1))
     hs = _stream(stream)
-    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, hs)
+    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, stream)
     st = lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
                             _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_quantize", st)
@@ -184,7 +208,7 @@ def nvfp4_qdq(x, g=None, out=None, stream=None):
     static = g is not None
     gg = g.reshape(1) if static else torch.empty(1, dtype=torch.float32, device=x.device)
     hs = _stream(stream)
-    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, hs)
+    ws = _quantize_ws(lib.nvfp4_quantize_workspace_size(rows, cols), x.device, stream)
     st = lib.nvfp4_qdq(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
                        _ptr(y), y.stride(0) if rows else cols, _ptr(gg), int(static), _ptr(ws),
                        ws.numel(), hs)
@@ -276,7 +300,7 @@ def nvfp4_fp8_quantize(x, g=None, out=None, stream=None):
     if static and gg.data_ptr() != g.data_ptr():
         gg.copy_(g.reshape(1))
     hs = _stream(stream)
-    ws = _quantize_ws(lib.nvfp4_fp8_quantize_workspace_size(rows, cols), x.device, hs)
+    ws = _quantize_ws(lib.nvfp4_fp8_quantize_workspace_size(rows, cols), x.device, stream)
     st = lib.nvfp4_fp8_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
                                 _ptr(q), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_fp8_quantize", st)

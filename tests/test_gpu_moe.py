@@ -77,6 +77,34 @@ def test_route_ties_and_signed_zero(B):
     _check_route(B, logits, 4)
 
 
+def test_route_nan_rows_stay_in_bounds(B):
+    """Router rows with NaN logits (fewer than k non-NaN ones, all-NaN rows
+    included): a NaN ranks as -infinity, so every token still gets k distinct
+    experts in [0, E) and the permutation stays a bijection; rows without NaN
+    route exactly as the oracle does."""
+    T, E, k = 300, 64, 8
+    logits = W.random_matrix(T, E, seed=77, device="cuda")
+    logits[0] = float("nan")
+    logits[5, 3:] = float("nan")
+    logits[9, ::2] = float("nan")
+    logits[100:164] = float("nan")
+    r = B.nvfp4_moe_route(logits, k)
+    torch.cuda.synchronize()
+    ids, offsets = _np(r["topk_ids"]), _np(r["offsets"]).astype(np.int64)
+    assert ids.min() >= 0 and ids.max() < E
+    assert all(len(set(row)) == k for row in ids)
+    assert list(ids[0]) == list(range(k))
+    assert offsets[0] == 0 and offsets[-1] == T * k and np.all(np.diff(offsets) >= 0)
+    np.testing.assert_array_equal(np.diff(offsets), np.bincount(ids.reshape(-1), minlength=E))
+    src, inv = _np(r["src_row"]), _np(r["inv"])
+    assert sorted(inv.reshape(-1)) == list(range(T * k))
+    np.testing.assert_array_equal(src[inv], np.repeat(np.arange(T), k).reshape(T, k))
+    lh = _np(logits)
+    clean = ~np.isnan(lh).any(axis=1)
+    ref_ids, _ = OM.route(lh[clean], k)
+    np.testing.assert_array_equal(ids[clean], ref_ids)
+
+
 def test_route_empty(B):
     r = B.nvfp4_moe_route(torch.zeros((0, 8), device="cuda"), 2)
     assert torch.all(r["offsets"] == 0)
@@ -115,7 +143,7 @@ def _routing(gen, T, E, k, device, skew=False):
     return logits
 
 
-def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True):
+def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True, out_dtype=torch.float32):
     dev = "cuda"
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -126,7 +154,7 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True):
     a = _rand_nvfp4(gen, (a_rows, H), dev)
     w = _rand_nvfp4(gen, (E, N, H), dev)
     out = B.nvfp4_moe_grouped_gemm(a, r["src_row"] if gather else None, r["offsets"], R, w,
-                                   epilogue=epi, out_dtype=torch.float32)
+                                   epilogue=epi, out_dtype=out_dtype)
     torch.cuda.synchronize()
     offsets = _np(r["offsets"]).astype(np.int64)
     src = _np(r["src_row"]) if gather else np.arange(R)
@@ -142,11 +170,13 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True):
                       np.float32(w[2][e].item()))
         if epi == B.NVFP4_EPI_SILU_GATE:
             ref = OM.silu_gate(ref)
-        got = _np(out[lo:hi]).astype(np.float64)
+        got = _np(out[lo:hi].float()).astype(np.float64)
+        if out_dtype == torch.bfloat16:
+            ref = _bf16_round(ref)
         err = OG.rel_fro_error(got, ref)
         errs.append(err)
         assert err <= TOL, (e, err)
-    print(f"[moe] grouped T={T} E={E} k={k} H={H} N={N} epi={epi}: experts checked {len(errs)}, "
+    print(f"[moe] grouped T={T} E={E} k={k} H={H} N={N} epi={epi} out={out_dtype}: experts checked {len(errs)}, "
           f"max rel err {max(errs):.2e}", flush=True)
     return out, offsets
 
@@ -171,6 +201,19 @@ def test_grouped_gemm_small(B, T, E, k, H, N, epi):
                                            (300, 6, 2, 1024, 2048, 0), (1000, 8, 2, 1024, 512, 1)])
 def test_grouped_gemm_two_tile_walk(B, T, E, k, H, N, epi):
     _grouped_case(B, T, E, k, H, N, epi, seed=T + E + N + epi)
+
+
+# bf16 output (what the layer stores) with each tile height the launcher picks:
+# about 256 rows per expert take 256-row tiles (2 x 2 waves), about 160 rows
+# 192-row tiles and about 60 rows 128-row tiles (1 x 4 waves); gated and not,
+# K with and without the two-tile walk.  Every expert checked against the
+# oracle rounded to bf16.
+@pytest.mark.parametrize("T,E,k,H,N,epi", [(4096, 16, 1, 512, 512, 1), (4096, 16, 1, 512, 512, 0),
+                                           (2560, 16, 1, 1024, 512, 1), (2560, 16, 1, 1024, 512, 0),
+                                           (960, 16, 1, 2048, 1024, 0), (960, 16, 1, 768, 512, 1),
+                                           (4096, 16, 1, 768, 1024, 0)])
+def test_grouped_gemm_bf16_out(B, T, E, k, H, N, epi):
+    _grouped_case(B, T, E, k, H, N, epi, seed=T + H + N + epi, out_dtype=torch.bfloat16)
 
 
 def test_grouped_gemm_without_gather(B):

@@ -297,3 +297,31 @@ def test_concurrent_streams_stay_exact(B):
             np.testing.assert_array_equal(q[sel].cpu().numpy(), rq)
     for k in keys:  # these workspaces were only for this test
         del B._QWS[k]
+
+
+def test_explicit_stream_not_current(B):
+    """stream= names a stream that is not torch's current one: the workspace is
+    allocated and zero-filled on that stream, so the first launch there sees the
+    fill; a larger tensor then grows the workspace on the same stream.  Codes,
+    scales and global scales bit-exact against the oracle."""
+    s = torch.cuda.Stream()
+    xs = [W.random_matrix(r, c, seed=500 + r, dtype=torch.bfloat16, device="cuda") * (2.0 + r)
+          for r, c in [(64, 256), (4096, 4096), (300, 1024)]]
+    torch.cuda.synchronize()
+    outs = []
+    for x in xs:
+        print(f"[quantize] explicit stream {tuple(x.shape)}", flush=True)
+        with torch.cuda.stream(s):
+            qo = (torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device="cuda"),
+                  torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device="cuda"),
+                  torch.empty(1, dtype=torch.float32, device="cuda"))
+        outs.append(B.nvfp4_quantize(x, out=qo, stream=s))
+    s.synchronize()
+    for x, (q, sc, g) in zip(xs, outs):
+        rq, rs, rg = Q.quantize(_host(x))
+        assert g.item() == rg
+        np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+        np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    key = (torch.cuda.current_device(), int(s.cuda_stream))
+    assert int(B._QWS[key][8:12].view(torch.int32).item()) == 0  # no expired waits
+    del B._QWS[key]

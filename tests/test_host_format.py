@@ -112,3 +112,51 @@ def test_fast_division(helper):
     cases = [(int(n), d) for d in ds for n in list(rng.integers(0, 2 ** 31, 200)) + [0, d - 1, d, 2 ** 31 - 1]]
     got = helper([f"div {n} {d}" for n, d in cases])
     assert [int(v) for v in got] == [n // d for n, d in cases]
+
+
+def _topk_host(helper, rows, k):
+    lines = [f"topk {r.shape[0]} {k} " + " ".join(_bits(r)) for r in rows]
+    return np.array([[int(v) for v in l.split()] for l in helper(lines)], dtype=np.int64)
+
+
+def test_topk_selection_matches_oracle_on_finite_rows(helper):
+    """The top-k kernel's ranking, run on the host, against the oracle's sort:
+    larger logit first, ties to the lower expert id (rows with many ties)."""
+    from oracle import moe as OM
+    rng = np.random.default_rng(6)
+    rows = rng.standard_normal((200, 40)).astype(np.float32)
+    rows[:50] = np.round(rows[:50])  # heavy ties
+    rows[50:60] = 0.0
+    rows[60, 5] = -0.0
+    rows[61] = -np.inf
+    rows[62, :7] = np.inf
+    ids, _ = OM.topk(np.where(np.isinf(rows), np.sign(rows) * 1e38, rows).astype(np.float32), 9)
+    got = _topk_host(helper, rows, 9)
+    np.testing.assert_array_equal(got[:61], ids[:61])
+    assert list(got[61]) == list(range(9))          # all -inf: lowest ids
+    assert list(got[62][:7]) == list(range(7))       # the seven +inf first
+
+
+def test_topk_selection_never_runs_out_on_nan_rows(helper):
+    """A NaN logit ranks as -infinity: a row with fewer than k non-NaN logits,
+    an all-NaN row included, still gets k distinct experts in [0, E), the
+    finite logits first in their order, then the NaN ones by lower id."""
+    rng = np.random.default_rng(7)
+    E, k = 64, 10
+    rows = rng.standard_normal((6, E)).astype(np.float32)
+    rows[0] = np.nan                                  # all NaN
+    rows[1, 3:] = np.nan                              # 3 finite logits, k = 10
+    rows[2, ::2] = np.nan                             # half NaN
+    rows[3, :] = np.nan
+    rows[3, 40] = -np.inf                             # -inf ties with NaN: lower id first
+    rows[4, 10:20] = np.nan                           # NaNs only among low ranks
+    got = _topk_host(helper, rows, k)
+    for r, ids in zip(rows, got):
+        assert len(set(ids)) == k and ids.min() >= 0 and ids.max() < E
+        fin = np.flatnonzero(~np.isnan(r) & ~np.isneginf(r))
+        nfin = min(k, fin.size)
+        order = sorted(fin, key=lambda e: (-r[e], e))[:nfin]
+        assert list(ids[:nfin]) == order
+    assert list(got[0]) == list(range(k))
+    assert list(got[1][3:]) == list(range(3, 10))
+    assert list(got[3]) == list(range(k))
