@@ -31,7 +31,7 @@
  *   - Calls on one stream are ordered; calls that share output or workspace
  *     buffers on different streams race.  The library keeps no global state
  *     other than per-device caches of the architecture check and the compute
- *     unit count.
+ *     unit count, and the per-GPU scratch array of nvfp4_quantize_noalloc.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -103,6 +103,24 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows,
                             int64_t cols, int64_t ld_x, uint8_t *q, uint8_t *s,
                             float *g, int static_global, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/* nvfp4_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * nvfp4_quantize; the scratch the dynamic mode needs (the single-read
+ * kernel's arrival state and at most 256 amax partials: 9472 bytes) is a
+ * device array inside the library, one per GPU, held until the process ends,
+ * so every shape nvfp4_quantize accepts fits (a request that would need more
+ * returns NVFP4_ERR_INVALID_ARG).  Nothing is allocated: the first call on a
+ * device looks up that device's copy of the array and zero-fills it with a
+ * kernel on `stream`; every completed call leaves it ready for the next.
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and may return wrong global
+ * scales; serialize them, or use nvfp4_quantize with separate workspaces. */
+nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype x_type,
+                                    int64_t rows, int64_t cols, int64_t ld_x,
+                                    uint8_t *q, uint8_t *s, float *g,
+                                    int static_global, hipStream_t stream);
 
 /* Batched dynamic quantize of `batch` independent matrices laid out
  * contiguously: x [batch][rows][cols] (dense), q [batch][rows][cols/2],

@@ -80,6 +80,55 @@ QuantParams make_quant(const void *x, int64_t rows, int64_t cols, int64_t ld, ui
   return p;
 }
 
+// Dynamic quantize on the device (validated arguments; workspace holds the
+// resident-kernel state followed by the amax partials).
+nvfp4_status quantize_impl(const void *x, nvfp4_dtype x_type, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t *q, uint8_t *s, float *g, int static_global, void *workspace,
+                           hipStream_t stream) {
+  const bool vec = aligned16(x) && (ld_x * (int64_t)dtype_size(x_type)) % 16 == 0;
+  ResidentState *rs = static_cast<ResidentState *>(workspace);
+  void *partials = workspace ? static_cast<uint8_t *>(workspace) + kResidentStateBytes : nullptr;
+  QuantParams p = make_quant(x, rows, cols, ld_x, q, s, g, partials, static_global ? 1 : 0);
+  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, rs, stream));
+}
+
+// ---------------------------------------------- allocation-free quantize
+// Scratch of nvfp4_quantize_noalloc: the resident kernel's arrival state and
+// the amax partials (at most kMaxPartials per tensor, whatever its size).
+// Every GPU the library runs on holds its own copy until the process ends.
+constexpr size_t kScratchBytes = kResidentStateBytes + (kMaxPartials * sizeof(float) + 255) / 256 * 256;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this device's scratch (the array's host-side name is a
+// stand-in that kernels cannot use), looked up once per device with that
+// device current.  The first call on a device also zero-fills it with a
+// kernel on the caller's stream, ordered before that call's own kernels;
+// after that every completed call leaves the arrival state ready for the
+// next.
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+
+__global__ void zero_scratch_kernel(uint32_t *p, uint32_t words) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+nvfp4_status device_scratch(void **out, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_UNSUPPORTED;
+  uintptr_t a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return NVFP4_ERR_HIP;
+    zero_scratch_kernel<<<1, 256, 0, stream>>>(static_cast<uint32_t *>(ptr), (uint32_t)(kScratchBytes / 4));
+    if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
+    a = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch[dev].store(a, std::memory_order_release);
+  }
+  *out = reinterpret_cast<void *>(a);
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,11 +163,23 @@ nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_type, int64_t rows, int
   }
   nvfp4_status st = check_device();
   if (st != NVFP4_OK) return st;
-  const bool vec = aligned16(x) && (ld_x * (int64_t)dtype_size(x_type)) % 16 == 0;
-  ResidentState *rs = static_cast<ResidentState *>(workspace);
-  void *partials = workspace ? static_cast<uint8_t *>(workspace) + kResidentStateBytes : nullptr;
-  QuantParams p = make_quant(x, rows, cols, ld_x, q, s, g, partials, static_global ? 1 : 0);
-  return from_hip(launch_quantize(p, x_type == NVFP4_BF16, vec, 1, rs, stream));
+  return quantize_impl(x, x_type, rows, cols, ld_x, q, s, g, static_global, workspace, stream);
+}
+
+nvfp4_status nvfp4_quantize_noalloc(const void *x, nvfp4_dtype x_type, int64_t rows, int64_t cols,
+                                    int64_t ld_x, uint8_t *q, uint8_t *s, float *g, int static_global,
+                                    hipStream_t stream) {
+  if (!valid_dtype(x_type) || !quant_shape_ok(rows, cols) || ld_x < cols || !g)
+    return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !q || !s)) return NVFP4_ERR_INVALID_ARG;
+  if (rows > 0 && ld_x > kI32Max * 64ll) return NVFP4_ERR_INVALID_ARG;
+  if (quant_ws(1, rows, cols, true) > kScratchBytes) return NVFP4_ERR_INVALID_ARG;
+  if (static_global && rows == 0) return NVFP4_OK;
+  nvfp4_status st = check_device();
+  if (st != NVFP4_OK) return st;
+  void *ws = nullptr;
+  if (!static_global && (st = device_scratch(&ws, stream)) != NVFP4_OK) return st;
+  return quantize_impl(x, x_type, rows, cols, ld_x, q, s, g, static_global, ws, stream);
 }
 
 size_t nvfp4_quantize_batched_workspace_size(int64_t batch, int64_t rows, int64_t cols) {

@@ -37,6 +37,8 @@ SIGNATURES = {
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quantize": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, ctypes.c_int,
                                       _P, _SZ, _P]),
+    "nvfp4_quantize_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P,
+                                              ctypes.c_int, _P]),
     "nvfp4_quantize_batched_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quantize_batched": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _P, _P,
                                               _SZ, _P]),
@@ -189,6 +191,32 @@ def nvfp4_quantize(x, g=None, out=None, stream=None):
     st = lib.nvfp4_quantize(_ptr(x), _dtype_code(x.dtype), rows, cols, x.stride(0) if rows else cols,
                             _ptr(q), _ptr(s), _ptr(gg), int(static), _ptr(ws), ws.numel(), hs)
     _check("nvfp4_quantize", st)
+    return q, s, gg
+
+
+def nvfp4_quantize_noalloc(x, g=None, out=None, stream=None):
+    """nvfp4_quantize through the allocation-free entry point: the library's own
+    per-GPU scratch replaces the workspace (calls overlapping on one GPU race).
+    Arguments and results as for :func:`nvfp4_quantize`; with ``out`` given,
+    nothing is allocated at all."""
+    lib = load_library()
+    _on_gpu(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along the last dim")
+    rows, cols = x.shape
+    if out is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+        gg = torch.empty(1, dtype=torch.float32, device=x.device)
+    else:
+        q, s, gg = out
+    static = g is not None
+    if static and gg.data_ptr() != g.data_ptr():
+        gg.copy_(g.reshape(1))
+    st = lib.nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x.dtype), rows, cols,
+                                    x.stride(0) if rows else cols, _ptr(q), _ptr(s), _ptr(gg),
+                                    int(static), _stream(stream))
+    _check("nvfp4_quantize_noalloc", st)
     return q, s, gg
 
 
