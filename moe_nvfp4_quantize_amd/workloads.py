@@ -105,8 +105,9 @@ def linear_inputs(name, device="cpu", M=None):
     raise KeyError(name)
 
 
-def moe_inputs(name, device="cpu", T=None, E=None, H=None, I=None, k=None, hot=None):
-    """dict(logits, x, w_gate_up, w_down, k) for an MoE workload; sizes overridable."""
+def moe_inputs(name, device="cpu", T=None, E=None, H=None, I=None, k=None, hot=None, weights=True):
+    """dict(logits, x, w_gate_up, w_down, k) for an MoE workload; sizes overridable.
+    ``weights=False`` stops after X (same logits and X; no expert weights)."""
     cfg = dict(WORKLOADS[name])
     for key, val in dict(T=T, E=E, H=H, I=I, k=k, hot=hot).items():
         if val is not None:
@@ -120,6 +121,8 @@ def moe_inputs(name, device="cpu", T=None, E=None, H=None, I=None, k=None, hot=N
         toks = torch.randperm(T, generator=gen, device=device)[:n_tok]
         logits[toks[:, None], hot_ids[None, :]] += 4.0
     x = _normal((T, H), 1.0, gen, device).to(torch.bfloat16)
+    if not weights:
+        return dict(logits=logits, x=x, k=k)
     w_gu = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=device)
     w_d = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
     # one expert at a time keeps the float32 temporaries small
