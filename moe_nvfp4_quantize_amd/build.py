@@ -3,7 +3,9 @@
     python -m moe_nvfp4_quantize_amd.build        # or: from ... import build; build.build()
 
 Every source is compiled to an object under ``_build/`` next to this file and
-linked into ``libnvfp4.so`` beside it.  The device code is built with:
+linked into ``libnvfp4.so`` beside it; the benchmark's HBM ceiling kernels
+(``csrc/ceiling.hip``, not part of the layer) go into ``libnvfp4_ceiling.so``.
+The device code is built with:
   * ``-ffp-contract=off``: the quantizer's float32 steps are specified one
     rounding at a time; no multiply-add fusion may merge them;
   * ``-fhip-fp32-correctly-rounded-divide-sqrt``: its two divisions per block
@@ -25,6 +27,8 @@ LIB = os.path.join(HERE, "libnvfp4.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "fp8_gemm.hip", "moe.hip"]
+CEILING_SOURCES = ["ceiling.hip"]
+LIB_CEILING = os.path.join(HERE, "libnvfp4_ceiling.so")
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -54,20 +58,27 @@ def _compile(src):
     return obj, warn
 
 
-def build(verbose=False):
-    """Compile every source and link libnvfp4.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for obj, warn in results:
-        if warn.strip() and verbose:
-            print(warn, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[o for o, _ in results]]
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every source and link libnvfp4.so (and libnvfp4_ceiling.so);
+    returns the path of libnvfp4.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = dict(zip(srcs, ex.map(_compile, srcs)))
+    for obj, warn in results.values():
+        if warn.strip() and verbose:
+            print(warn, file=sys.stderr)
+    _link([results[s][0] for s in SOURCES], LIB)
+    _link([results[s][0] for s in CEILING_SOURCES], LIB_CEILING)
     return LIB
 
 
