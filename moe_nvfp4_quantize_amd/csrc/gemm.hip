@@ -536,17 +536,17 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     origin(0, &row0, &row_end, &tile_n);
     b_g = *p.b_g;
   } else {
-    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM).
-    // Workgroup b runs on XCD b % 8: XCD x takes M tiles x, x + 8, x + 16, ...,
-    // each with all its N tiles in a row, so that the gathered rows of an M tile
-    // are fetched into one L2, and the M tiles past the last real one (the grid
-    // covers an upper bound, a multiple of 8 M tiles) leave every XCD alike.
-    // (with the walk: N tiles 2j and 2j + 1 of the M tile, one after the other)
+    // tile_mm-th M tile over all experts, expert e contributing ceil(n_e / BM);
+    // a work item is one N tile of an M tile (with the walk: N tiles 2j and
+    // 2j + 1, one after the other).  Workgroup b runs on XCD b % 8, and XCD x
+    // takes the contiguous run of items [x n / 8, (x + 1) n / 8) of the n real
+    // items in M-major order (n is known once the scan below has counted the
+    // experts' tiles; the grid covers an upper bound): every XCD gets the same
+    // share of the real work, the N tiles of an M tile run back to back on one
+    // XCD (its gathered rows fetched into that L2 once), and so do the M tiles of
+    // one expert, whose weight panels its L2 then serves to both.
     const uint32_t tpw = gwalk ? 2u : 1u, npairs = tiles_n / tpw;
     my_tiles = tpw;
-    const uint32_t wl = blockIdx.x / 8;
-    tile_n = (wl % npairs) * tpw;
-    const uint32_t tile_mm = 8 * (wl / npairs) + blockIdx.x % 8;
     if (tid == 0) sInfo[0] = -1;
     // Exclusive prefix over experts of ceil(n_e / BM) in one pass: thread t owns
     // experts [t * per, t * per + per); a scan of the threads' sums inside each
@@ -565,6 +565,15 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     __syncthreads();
     uint32_t first = incl - own;  // M tiles before this thread's first expert
     for (uint32_t w = 0; w < wave; ++w) first += scan[w];
+    const uint32_t items = (scan[0] + scan[1] + scan[2] + scan[3]) * npairs;
+    const uint32_t xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    const uint32_t it0 = (uint32_t)((uint64_t)xcd * items / 8), it1 = (uint32_t)((uint64_t)(xcd + 1) * items / 8);
+    uint32_t tile_mm = 0xFFFFFFFFu;  // past the real items: no thread matches
+    tile_n = 0;
+    if (local < it1 - it0) {
+      tile_mm = (it0 + local) / npairs;
+      tile_n = ((it0 + local) % npairs) * tpw;
+    }
     if (tile_mm >= first && tile_mm < first + own) {
       for (uint32_t e = e_lo; e < e_hi; ++e) {
         const uint32_t lo = (uint32_t)p.expert_offsets[e];
