@@ -214,3 +214,20 @@ def test_deterministic(B):
     y1 = B.nvfp4_gemm(qa, qb)
     y2 = B.nvfp4_gemm(qa, qb)
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("g_exp", [-4, -130])
+def test_bf16_output_is_rounded_f32_output(B, g_exp):
+    """The bf16 epilogue stores the float32 result rounded to nearest even,
+    bit for bit, subnormal results included (tiny global scales): the same
+    operands through the float32 and the bf16 output paths."""
+    rng = np.random.default_rng(17 - g_exp)
+    a = _random_nvfp4(rng, 300, 1024, 2.0 ** g_exp)
+    b = _random_nvfp4(rng, 520, 1024, 2.0 ** -6)
+    y32 = _run(B, a, b, torch.float32)
+    y16 = _run(B, a, b, torch.bfloat16)
+    torch.cuda.synchronize()
+    want = y32.cpu().to(torch.bfloat16)
+    assert torch.equal(y16.cpu().view(torch.int16), want.view(torch.int16))
+    if g_exp < -126:
+        assert (y32.abs() < 2.0 ** -126).float().mean().item() > 0.05  # many subnormal results

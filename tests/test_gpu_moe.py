@@ -349,6 +349,22 @@ def test_combine(B, T, k, H, y_bf16):
     np.testing.assert_allclose(_np(out32), ref, rtol=1e-5, atol=1e-5)
 
 
+def test_combine_bf16_output_is_rounded_f32_output(B):
+    """bf16 output = the float32 combine rounded to nearest even, bit for bit,
+    subnormal sums included."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    T, k, H = 64, 8, 4096
+    y = torch.randn((T * k, H), generator=gen, device="cuda")
+    y[: T * k // 2] *= 2.0 ** -130  # subnormal products
+    w = torch.rand((T, k), generator=gen, device="cuda")
+    inv = torch.randperm(T * k, generator=gen, device="cuda").to(torch.int32).reshape(T, k)
+    o32 = B.nvfp4_moe_combine(y, w, inv, out_dtype=torch.float32)
+    o16 = B.nvfp4_moe_combine(y, w, inv, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16.cpu().view(torch.int16), o32.cpu().to(torch.bfloat16).view(torch.int16))
+
+
 # ------------------------------------------------------------- end to end
 
 
