@@ -48,6 +48,8 @@ namespace nvfp4 {
 namespace {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -826,38 +828,57 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
   auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf) {
+    // The lane's index, computed afresh here: lane-derived addresses kept live
+    // across the K loop for the epilogue get spilled, and each reload waits for
+    // every transfer in flight, including the next tile's first steps.
+    uint32_t ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const uint32_t el32 = ln % 32, elh = ln / 32;
     uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
     const uint32_t col0 = tn * BN_OUT + wn * WN_OUT;
+    // output value of accumulator register r of fragments (i, j) (with the
+    // gate: of gate fragment j and its up fragment j + HALF)
+    auto value = [&](int i, int j, int r) -> float {
+      if constexpr (SILU) return silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale);
+      else return acc[i][j][r] * out_scale;
+    };
+    constexpr int NJ = SILU ? HALF : FN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if ((uint32_t)i >= nf) break;  // rows past the tile's end: nothing to write
 #pragma unroll
       for (int ps = 0; ps < 32 / RPP; ++ps) {
 #pragma unroll
-        for (int r = ps * (RPP / 2); r < (ps + 1) * (RPP / 2); ++r) {
-          // one accumulator register at a time: the tile's live pipeline state
-          // leaves few free registers here
+        for (int r = ps * (RPP / 2); r < (ps + 1) * (RPP / 2); r += 2) {
+          // registers r and r + 1: rows tr and tr + 1 of the lane's column
           __builtin_amdgcn_sched_barrier(0);
-          const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4) - ps * RPP;
-          OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
-          if (SILU) {
+          const uint32_t tr = 8 * (r / 4) + 4 * elh + (r % 4) - ps * RPP;
+          uint8_t *row = slab + tr * ROW_BYTES;
 #pragma unroll
-            for (int j = 0; j < HALF; ++j)
-              dst[j * 32 + l32] =
-                  to_out<OutT>(silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale));
-          } else {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * out_scale);
+          for (int j = 0; j < NJ; ++j) {
+            const float v0 = value(i, j, r), v1 = value(i, j, r + 1);
+            if constexpr (sizeof(OutT) == 2) {
+              // both rounded to nearest even by one packed convert
+              const float2v f = {v0, v1};
+              const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+              reinterpret_cast<uint16_t *>(row)[j * 32 + el32] = (uint16_t)pk;
+              reinterpret_cast<uint16_t *>(row + ROW_BYTES)[j * 32 + el32] = (uint16_t)(pk >> 16);
+            } else {
+              reinterpret_cast<float *>(row)[j * 32 + el32] = v0;
+              reinterpret_cast<float *>(row + ROW_BYTES)[j * 32 + el32] = v1;
+            }
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        // the slab is this wave's own: ordering inside the wave suffices (a
+        // workgroup-scope fence would also wait for every load in flight)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         const uint32_t rbase = r0 + (NWM * i + wm) * 32 + ps * RPP;
         if constexpr (QOUT) {
           // NVFP4 output with the static global scale: one 16-element block per
           // lane (RPP rows x ROW_ELEMS / 16 blocks), the quantizer's arithmetic
           static_assert(RPP * (ROW_ELEMS / 16) == 64, "one block per lane");
-          const uint32_t tr = lane / (ROW_ELEMS / 16), bk = lane % (ROW_ELEMS / 16);
+          const uint32_t tr = ln / (ROW_ELEMS / 16), bk = ln % (ROW_ELEMS / 16);
           const uint32_t row = rbase + tr, col = col0 + bk * 16;
           if (row < row_end && col < n_out) {
             const u32x4 *hv = reinterpret_cast<const u32x4 *>(slab + tr * ROW_BYTES + bk * 64);
@@ -891,20 +912,29 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
           __builtin_amdgcn_wave_barrier();
           continue;
         }
-        // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk
+        // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk:
+        // every chunk of the pass is read from LDS first, then all are stored
         constexpr int VEC = 16 / (int)sizeof(OutT);
         constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
-        for (int c = lane; c < RPP * CPR; c += 64) {
-          const uint32_t tr = c / CPR, cc = c % CPR;
-          const uint32_t row = rbase + tr;
-          const uint32_t col = col0 + cc * VEC;
-          if (row >= row_end) continue;
-          const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
+        constexpr int NCH = RPP * CPR, NIT = (NCH + 63) / 64;
+        u32x4 chunk[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const uint32_t c = ln + it * 64;
+          if (NCH % 64 == 0 || c < (uint32_t)NCH)
+            chunk[it] = *reinterpret_cast<const u32x4 *>(slab + (c / CPR) * ROW_BYTES + (c % CPR) * 16);
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const uint32_t c = ln + it * 64;
+          const uint32_t row = rbase + c / CPR, col = col0 + (c % CPR) * VEC;
+          if ((NCH % 64 != 0 && c >= (uint32_t)NCH) || row >= row_end) continue;
           OutT *gp = C + (int64_t)row * p.ldc + col;
           if (VSTORE && col + VEC <= n_out) {
-            *reinterpret_cast<u32x4 *>(gp) = *reinterpret_cast<const u32x4 *>(srcp);
+            *reinterpret_cast<u32x4 *>(gp) = chunk[it];
           } else {
-            const OutT *sv = reinterpret_cast<const OutT *>(srcp);
+            OutT sv[VEC];
+            __builtin_memcpy(sv, &chunk[it], 16);
             for (int e = 0; e < VEC; ++e)
               if (col + e < n_out) gp[e] = sv[e];
           }
@@ -1081,7 +1111,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     // the tile is done: the next tile's first steps are already in flight
     wait_lgkm0();
     epilogue(g - 1, row0, tile_n, nf);
-    __syncthreads();  // staging done before the next step's transfers
+    // every wave's staging reads done before the next step's transfers rewrite
+    // the stage (no wait for the transfers in flight: they fill other stages)
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
