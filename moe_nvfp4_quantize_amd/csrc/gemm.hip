@@ -794,14 +794,23 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa8[i], ob8[j], acc[i][j], 0, 0, 0);
   };
   // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), FM * FN
-  // times; NV memory transfers spread evenly
-  auto interleave = [&](auto f_tag, auto nv_tag) {
+  // times; NV memory transfers and ND LDS reads spread evenly.  The reads of a
+  // half step's operands go between its first MFMAs: issued as one burst right
+  // after a barrier, the four waves' reads queue behind each other and hold up
+  // the MFMAs (2-3% of the prefill GEMM's time)
+  auto interleave = [&](auto f_tag, auto nv_tag, auto nd_tag) {
     constexpr int F = decltype(f_tag)::value;
     constexpr int NV = decltype(nv_tag)::value, NM = F * FN;
+    constexpr int ND = decltype(nd_tag)::value;
     constexpr int VPM = (8 * (F + FN) + NM - 1) / NM;
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (ND > 0) {
+        const int nd = ((k + 1) * ND) / NM - (k * ND) / NM;
+#pragma unroll
+        for (int v = 0; v < nd; ++v) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
       if constexpr (NV > 0 && NM >= NV) {
         if (k % (NM / NV) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -1024,7 +1033,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       }
       u32x4 ha[FM], hb[FN];
       if constexpr (F > 0) read_half(ft, g, 1, ha, hb);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if constexpr (F > 0) {
@@ -1036,10 +1044,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
         if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, (part % 4) % TA, part % 4);
         if constexpr (F > 0) {
-          if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>());
-          if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>());
-          if (t == 2) interleave(ft, std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>());
-          if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>());
+          if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>(), std::integral_constant<int, F + FN>());
+          if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
+          if (t == 2) interleave(ft, std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
+          if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>(), std::integral_constant<int, 0>());
         }
       }
       // step g + 1 has landed: at most the transfers issued since the
@@ -1055,7 +1063,6 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         read_half(ft, g + 1, 0, fa, fb);
         read_scales(ft, ti * cpt + nks / SC_STEPS, nks, na, nb);
       }
-      __builtin_amdgcn_sched_barrier(0);
       half2v npa[FM][2], npb[FN][2];
       if constexpr (F > 0) {
 #pragma unroll
@@ -1072,7 +1079,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
             pairs(ft, na, nb, npa, npb);
             decode_step(ft, 0, fa, fb, npa, npb, av[0], bv[0]);
           }
-          interleave(ft, std::integral_constant<int, 0>());
+          if (t == 4) interleave(ft, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * (F + FN)>());
+          else interleave(ft, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
         }
       }
 #pragma unroll
