@@ -54,6 +54,7 @@ typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 128;        // K elements per stage
 constexpr int KB = BK / 2;     // packed bytes per row per stage
@@ -443,12 +444,15 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
 //  * Decode is software pipelined: while the MFMAs of sub-step t run (16 for
 //    256-row tiles), the operands of sub-step t + 1 are decoded (one MFMA, then
 //    a few VALU instructions, in turn).
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2,
+          int BN = 256>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
-  // NWM x NWN waves: 2 x 2 (waves of BM/2 x 128) or 1 x 4 (BM x 64)
+  // NWM x NWN waves: 2 x 2 (waves of BM/2 x BN/2) or 1 x 4 (BM x BN/4)
   constexpr int NWN = 4 / NWM;
-  constexpr int BN = 256, WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32, HALF = FN / 2;
+  constexpr int WM = BM / NWM, WN = BN / NWN, FM = WM / 32, FN = WN / 32, HALF = FN / 2;
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile height");
+  static_assert(BN == 256 || (BN == 320 && BM == 128 && NWM == 2 && !GROUPED),
+                "320-column tiles: dense products of at most 128 rows, 2 x 2 waves of 64 x 160");
   static_assert(NWM == 1 || NWM == 2, "wave grid");
   static_assert(FM <= 8, "at most eight A fragments per wave");
   static_assert(!QOUT || NWM == 2, "the NVFP4 epilogue quantizes 64-column wave slabs");
@@ -456,11 +460,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   static_assert(!QOUT || (SILU && sizeof(OutT) == 4), "NVFP4 output: SiLU-gate epilogue, f32 staging");
   // transfers (64 lanes x 16 bytes) per operand: per code stage, and per scale chunk
   constexpr int TA = BM / 64, TB = BN / 64, TN = TA + TB;
-  // code stages: [A BM rows x 64 B][B 256 rows x 64 B], fetched AHEAD steps
-  // ahead: four stages for 128-row tiles (skinny products stream their weights
-  // from HBM, so the fetch has to run further ahead; 144 KB of LDS), three
-  // otherwise (a fourth would not fit)
-  constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = BM == 128 ? 4 : 3;
+  // scale transfers per K step: one of A, NSB of B (a chunk's TB transfers of
+  // B spread over its first four steps)
+  constexpr int NSB = (TB + 3) / 4, NSC = 1 + NSB;
+  // code stages: [A BM rows x 64 B][B BN rows x 64 B], fetched AHEAD steps
+  // ahead: four stages for 128 x 256 tiles (skinny products stream their
+  // weights from HBM, so the fetch has to run further ahead; 144 KB of LDS),
+  // three otherwise (a fourth would not fit)
+  constexpr int CODE_B = BM * 64, CODE_STAGE = (BM + BN) * 64, NSTAGE = (BM == 128 && BN == 256) ? 4 : 3;
   constexpr int AHEAD = NSTAGE - 1;
   // scale chunks: the scales of SC_STEPS K steps, [A BM rows x 64 B][B ...], two of them
   constexpr int SC_STEPS = 8, SC_B = BM * 64, SC_CHUNK = (BM + BN) * 64;
@@ -639,7 +646,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // the full offset of the gathered row (base 0, no clamp).  Offsets fit 32
   // bits (checked by the host).
   const uint32_t pc = (tid % 4) ^ swz(tid / 4);
-  u32x4 la = {0, 0, 0, 0}, lb, lsa = {0, 0, 0, 0}, lsb;
+  // (vectors, not arrays: an index known only at run time becomes selects)
+  typedef std::conditional_t<(TB > 4), u32x8, u32x4> BOffsets;
+  u32x4 la = {0, 0, 0, 0}, lsa = {0, 0, 0, 0};
+  BOffsets lb, lsb;
   uint32_t last_a, last_b, last_sa, last_sb;
   if (!GROUPED) {
 #pragma unroll
@@ -691,17 +701,23 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + off), (lds_void *)(st + CODE_B + (q - TA) * 4096 + wave * 1024), 16, 0, 0);
     }
   };
-  // scale transfers of chunk c of the tile at (ar, bc), into the buffer of
-  // global chunk gc: A transfer ja and B transfer jb (possibly not known at
-  // compile time: vector selects, no indexing into memory).  A piece past the
-  // end of the row reloads the chunk's first piece instead (K % 256 == 0
-  // keeps that in the row).
-  auto issue_scales = [&](uint32_t gc, uint32_t c, uint32_t ar, uint32_t bc, uint32_t ja, uint32_t jb) {
+  // scale transfers of part q (0..3) of chunk c of the tile at (ar, bc), into
+  // the buffer of global chunk gc: A transfer q % TA and B transfers q, q + 4,
+  // ... (the last one repeated past TB; q possibly not known at compile time:
+  // vector selects, no indexing into memory).  A piece past the end of the row
+  // reloads the chunk's first piece instead (K % 256 == 0 keeps that in the row).
+  auto issue_scales = [&](uint32_t gc, uint32_t c, uint32_t ar, uint32_t bc, uint32_t q) {
     uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + wave * 1024;
     const uint32_t back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16;
-    const uint32_t oa = min(lsa[ja] + ar * kscales, last_sa), ob = min(lsb[jb] + bc * kscales, last_sb);
+    const uint32_t ja = q % TA;
+    const uint32_t oa = min(lsa[ja] + ar * kscales, last_sa);
     __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + oa - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      const uint32_t jb = min(q + 4 * sb, (uint32_t)TB - 1);
+      const uint32_t ob = min(lsb[jb] + bc * kscales, last_sb);
+      __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
+    }
   };
 
   const uint32_t wm = wave / NWN, wn = wave % NWN;
@@ -960,7 +976,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // read from LDS while this step's second half is multiplied.  Codes are
   // fetched AHEAD steps ahead (across a tile boundary: the next tile's first
   // steps); scale chunk c + 1 (or the next tile's chunk 0) during the first
-  // four steps of chunk c.  Every step issues TN + 2 transfers (near the end
+  // four steps of chunk c.  Every step issues TN + NSC transfers (near the end
   // the last step's codes again, into a stage nobody reads any more; outside
   // the first four steps of a chunk the current chunk's scales again,
   // rewriting identical bytes), so at the mid-step barrier one wait count
@@ -969,7 +985,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   uint32_t nrow0 = row0, nrow_end = row_end, ntile_n = tile_n;  // the tile after the current one
   if (my_tiles > 1) origin(1, &nrow0, &nrow_end, &ntile_n);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j % TA, j);
+  for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j);
   // steps 0 .. AHEAD - 1 (a short single tile reloads its last step into the
   // stages past it, which nobody reads; a walk of several tiles has at least 8
   // steps per tile)
@@ -1042,17 +1058,17 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
 #pragma unroll
         for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
-        if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, (part % 4) % TA, part % 4);
+        if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, part % 4);
         if constexpr (F > 0) {
           if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>(), std::integral_constant<int, F + FN>());
           if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
           if (t == 2) interleave(ft, std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
-          if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + 2>(), std::integral_constant<int, 0>());
+          if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + NSC>(), std::integral_constant<int, 0>());
         }
       }
       // step g + 1 has landed: at most the transfers issued since the
       // fetch of step g + 1 (the last AHEAD - 1 steps' codes, and scales) remain
-      wait_vm<(AHEAD - 1) * TN + 2>();
+      wait_vm<(AHEAD - 1) * TN + NSC>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -1182,10 +1198,40 @@ uint32_t dense_grid(const GemmParams &p, uint32_t tiles, uint32_t bm) {
   return g == 0 || tiles <= g ? tiles : g;
 }
 
-template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2>
+template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2,
+          int BN = 256>
 hipError_t launch_dma(const GemmParams &p, uint32_t grid, hipStream_t stream) {
-  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT, QOUT, NWM><<<grid, 256, 0, stream>>>(p);
+  gemm_dma_kernel<BM, GROUPED, SILU, VSTORE, OutT, QOUT, NWM, BN><<<grid, 256, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+// Tile width for dense products of at most 128 rows: one tile row, so the
+// column tiles are the whole schedule, one workgroup per compute unit.  A
+// product whose 256-column tiles leave a partly filled last round (run as row
+// halves, at about 0.8 of a round: a half tile still decodes most of a full
+// tile's operands) can take 320-column tiles (2 x 2 waves of 64 x 160) in
+// fewer rounds: lm_head 128 x 151936 needs 594 tiles of 256 (2.32 rounds, run
+// in about 2.8) or 475 of 320 (two rounds).  The cost compared is rounds x
+// width; 320 only with more than 32 rows (with fewer, a 2 x 2 tile leaves its
+// second wave row idle).
+int skinny_tile_width(const GemmParams &p) {
+  const uint32_t cu = device_cu_count() & ~7u;
+  if (cu == 0 || p.M <= 32) return 256;
+  const bool halves = p.M > 64, persistent = (p.K / 128) % 8 == 0;
+  auto cost = [&](uint32_t bn) {
+    const uint32_t tiles = (p.N + bn - 1) / bn;
+    double rounds;
+    if (2 * tiles <= cu && halves) {
+      rounds = 0.8;
+    } else if (tiles <= cu) {
+      rounds = 1.0;
+    } else {
+      const uint32_t full = tiles / cu, rem = tiles % cu;
+      rounds = full + (rem == 0 ? 0.0 : (persistent && 2 * rem <= cu && halves ? 0.8 : 1.0));
+    }
+    return rounds * bn;
+  };
+  return cost(320) < 0.95 * cost(256) ? 320 : 256;
 }
 
 // Tile height for the grouped GEMM from the mean rows per expert m = R / E.
@@ -1248,18 +1294,23 @@ hipError_t launch_gemm(const GemmParams &p, OutType out, hipStream_t stream) {
     // halves decodes 4 fragments per 4 MFMAs instead of 5 (2 x 2 waves).
     // Measured against 2 x 2 on one host: lm_head 128x151936x2048 97.5 -> 95.5
     // us; M x 32768 x 4096 at M = 32 / 64 / 128: 44 -> 35, 47 -> 42, 51 -> 45 us.
-    auto go = [&](auto bm_tag) -> hipError_t {
-      constexpr int TBM = decltype(bm_tag)::value;
-      const uint32_t tiles = ((p.N + BN - 1) / BN) * ((p.M + TBM - 1) / TBM);
+    // Where 320-column tiles take fewer rounds (skinny_tile_width), those run
+    // instead, 2 x 2: lm_head 101 -> 96 us, bit-identical output.
+    auto go = [&](auto bm_tag, auto bn_tag) -> hipError_t {
+      constexpr int TBM = decltype(bm_tag)::value, TBN = decltype(bn_tag)::value;
+      const uint32_t tiles = ((p.N + TBN - 1) / TBN) * ((p.M + TBM - 1) / TBM);
       const uint32_t g = dense_grid(p, tiles, TBM);
-      constexpr int W = TBM == 128 ? 1 : 2;
+      constexpr int W = (TBM == 128 && TBN == 256) ? 1 : 2;
       if (out == OutType::BF16)
-        return vs ? launch_dma<TBM, false, false, true, uint16_t, false, W>(p, g, stream)
-                  : launch_dma<TBM, false, false, false, uint16_t, false, W>(p, g, stream);
-      return vs ? launch_dma<TBM, false, false, true, float, false, W>(p, g, stream)
-                : launch_dma<TBM, false, false, false, float, false, W>(p, g, stream);
+        return vs ? launch_dma<TBM, false, false, true, uint16_t, false, W, TBN>(p, g, stream)
+                  : launch_dma<TBM, false, false, false, uint16_t, false, W, TBN>(p, g, stream);
+      return vs ? launch_dma<TBM, false, false, true, float, false, W, TBN>(p, g, stream)
+                : launch_dma<TBM, false, false, false, float, false, W, TBN>(p, g, stream);
     };
-    return p.M <= 128 ? go(std::integral_constant<int, 128>()) : go(std::integral_constant<int, BM>());
+    if (p.M > 128) return go(std::integral_constant<int, BM>(), std::integral_constant<int, BN>());
+    if (skinny_tile_width(p) == 320)
+      return go(std::integral_constant<int, 128>(), std::integral_constant<int, 320>());
+    return go(std::integral_constant<int, 128>(), std::integral_constant<int, 256>());
   }
   return out == OutType::BF16
              ? launch_cfg<BM, BN, 128, 128, false, false, uint16_t>(p, grid, al, vs, stream)

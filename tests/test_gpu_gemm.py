@@ -85,7 +85,7 @@ def _exact_operands(rng, rows, K):
     return Q.pack_codes(codes), s, np.float32(1.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 96, 256), (130, 70, 512), (7, 33, 48)])
+@pytest.mark.parametrize("M,N,K", [(64, 96, 256), (130, 70, 512), (7, 33, 48), (128, 76800, 256)])
 def test_exact_sums_are_bit_identical(B, M, N, K):
     rng = np.random.default_rng(M + N + K)
     a, b = _exact_operands(rng, M, K), _exact_operands(rng, N, K)
@@ -137,7 +137,7 @@ def _random_nvfp4(rng, rows, K, g):
 # halves of rows, and a product of at most 128 tiles runs every tile that way.
 @pytest.mark.parametrize("M,N,K,out_dtype", [
     (1000, 17000, 1024, torch.float32),   # 268 tiles: 12 split, ragged last rows 768..999
-    (100, 70000, 1024, torch.bfloat16),   # 274 tiles of 128 rows: 18 split, halves of 64 and 36 rows
+    (100, 90000, 1024, torch.bfloat16),   # 352 tiles of 128 rows: 96 split, halves of 64 and 36 rows
     (100, 3000, 1024, torch.float32),     # 12 tiles, all split
     (65, 1000, 1024, torch.float32),      # second halves hold one row
     (129, 700, 256, torch.bfloat16),      # 256-row tiles, K with no persistent walk
@@ -164,6 +164,19 @@ def test_random_shapes_full_output(B, M, N, K):
     out_dtype = torch.bfloat16 if (M + N) % 2 else torch.float32
     y = _run(B, a, b, out_dtype)
     _compare(y, G.gemm(*a, *b), out_dtype, f"random {M}x{N}x{K}")
+
+
+# Products of at most 128 rows whose 256-column tiles would leave a partly
+# filled last round run on 320-column tiles (2 x 2 waves of 64 x 160) when that
+# takes fewer rounds of a 256-CU device: one launch per tile (K % 1024 != 0) or
+# a persistent walk, ragged N, 33..64 rows (one 32-row group per wave row).
+@pytest.mark.parametrize("M,N,K", [(128, 76800, 256), (100, 70001, 512), (37, 76837, 1024), (65, 160000, 2048)])
+def test_wide_skinny_tiles_full_output(B, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    a, b = _random_nvfp4(rng, M, K, 2.0 ** -5), _random_nvfp4(rng, N, K, 2.0 ** -7)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        y = _run(B, a, b, out_dtype)
+        _compare(y, G.gemm(*a, *b), out_dtype, f"320-column tiles {M}x{N}x{K}")
 
 
 def test_output_row_stride(B):
