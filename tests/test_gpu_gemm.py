@@ -20,6 +20,8 @@ from oracle import nvfp4 as Q
 from oracle.formats import e2m1_decode
 from moe_nvfp4_quantize_amd import workloads as W
 
+import oracle_pool as OP
+
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
@@ -45,16 +47,29 @@ def _host(t):
     return t.detach().float().cpu().numpy()
 
 
-def _compare(y_gpu, y_ref, out_dtype, label):
+def _compare(y_gpu, y_ref, out_dtype, label, operands=None):
+    """Relative Frobenius error against the oracle (bf16-rounded for bf16
+    outputs) within TOL; with the operands (a, b) also every element within the
+    float32 accumulation bound (K/16 + 20) 2^-24 |a_m| |b_n| (plus one bf16
+    unit of the exact value for bf16 outputs, tests/oracle_pool.py)."""
     y = y_gpu.double().cpu().numpy()
     raw = G.rel_fro_error(y, y_ref)
     if out_dtype == torch.bfloat16:
         err = G.rel_fro_error(y, _bf16_round(y_ref))
     else:
         err = raw
-    print(f"[gemm] {label}: rel_fro={err:.3e} (vs raw fp64 {raw:.3e})", flush=True)
+    extra = ""
+    if operands is not None:
+        a, b = operands
+        K = a[0].shape[1] * 2
+        bound = (K / 16 + 20) * OP.U * np.outer(OP._row_norms(a), OP._row_norms(b))
+        st = OP._stats(y, y_ref, bound, out_dtype == torch.bfloat16)
+        extra = f", element-wise: {st['bad']} of {st['n']} past the bound (max ratio {st['max_ratio']:.3f})"
+    print(f"[gemm] {label}: rel_fro={err:.3e} (vs raw fp64 {raw:.3e}){extra}", flush=True)
     assert np.all(np.isfinite(y))
     assert err <= TOL, (label, err)
+    if operands is not None:
+        assert st["bad"] == 0, (label, st["bad"], st["max_ratio"])
     return err
 
 
@@ -122,7 +137,7 @@ def test_ragged_shapes(B, M, N, K, out_dtype):
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     a, b = Q.quantize(x), Q.quantize(w)
     y = _run(B, a, b, out_dtype)
-    _compare(y, G.gemm(*a, *b), out_dtype, f"ragged {M}x{N}x{K}")
+    _compare(y, G.gemm(*a, *b), out_dtype, f"ragged {M}x{N}x{K}", operands=(a, b))
 
 
 def _random_nvfp4(rng, rows, K, g):
@@ -148,7 +163,7 @@ def test_split_tile_walks_full_output(B, M, N, K, out_dtype):
     rng = np.random.default_rng(M + N + K)
     a, b = _random_nvfp4(rng, M, K, 2.0 ** -4), _random_nvfp4(rng, N, K, 2.0 ** -6)
     y = _run(B, a, b, out_dtype)
-    _compare(y, G.gemm(*a, *b), out_dtype, f"walk {M}x{N}x{K}")
+    _compare(y, G.gemm(*a, *b), out_dtype, f"walk {M}x{N}x{K}", operands=(a, b))
 
 
 # Seeded random shapes (K from 256 to 3072, M up to 700, N up to 40000) plus
@@ -163,7 +178,7 @@ def test_random_shapes_full_output(B, M, N, K):
     a, b = _random_nvfp4(rng, M, K, 2.0 ** -5), _random_nvfp4(rng, N, K, 2.0 ** -7)
     out_dtype = torch.bfloat16 if (M + N) % 2 else torch.float32
     y = _run(B, a, b, out_dtype)
-    _compare(y, G.gemm(*a, *b), out_dtype, f"random {M}x{N}x{K}")
+    _compare(y, G.gemm(*a, *b), out_dtype, f"random {M}x{N}x{K}", operands=(a, b))
 
 
 # Products of at most 128 rows whose 256-column tiles would leave a partly
@@ -176,7 +191,7 @@ def test_wide_skinny_tiles_full_output(B, M, N, K):
     a, b = _random_nvfp4(rng, M, K, 2.0 ** -5), _random_nvfp4(rng, N, K, 2.0 ** -7)
     for out_dtype in (torch.bfloat16, torch.float32):
         y = _run(B, a, b, out_dtype)
-        _compare(y, G.gemm(*a, *b), out_dtype, f"320-column tiles {M}x{N}x{K}")
+        _compare(y, G.gemm(*a, *b), out_dtype, f"320-column tiles {M}x{N}x{K}", operands=(a, b))
 
 
 def test_output_row_stride(B):
@@ -186,7 +201,7 @@ def test_output_row_stride(B):
     big = torch.full((20, 48), 7.0, device="cuda")
     B.nvfp4_gemm(_up(a), _up(b), out=big[:, :30])
     torch.cuda.synchronize()
-    _compare(big[:, :30], G.gemm(*a, *b), torch.float32, "ldc 48")
+    _compare(big[:, :30], G.gemm(*a, *b), torch.float32, "ldc 48", operands=(a, b))
     assert torch.all(big[:, 30:] == 7.0)
 
 

@@ -27,6 +27,8 @@ from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from moe_nvfp4_quantize_amd import workloads as W
 
+import oracle_pool as OP
+
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
 
@@ -162,7 +164,7 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True, out_dty
     src = _np(r["src_row"]) if gather else np.arange(R)
     experts = range(E) if sample is None else sample
     a_np = (_np(a[0]), _np(a[1]), np.float32(a[2][0].item()))
-    errs = []
+    errs, worst = [], 0.0
     for e in experts:
         lo, hi = offsets[e], offsets[e + 1]
         if hi == lo:
@@ -178,8 +180,15 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True, out_dty
         err = OG.rel_fro_error(got, ref)
         errs.append(err)
         assert err <= TOL, (e, err)
+        # every element within the float32 accumulation bound (tests/oracle_pool.py)
+        a_e = (a_np[0][rows], a_np[1][rows], a_np[2])
+        b_e = (_np(w[0][e]), _np(w[1][e]), np.float32(w[2][e].item()))
+        check = OP.silu_gate_block_check if epi == B.NVFP4_EPI_SILU_GATE else OP.gemm_block_check
+        st = check(a_e, b_e, got, out_dtype == torch.bfloat16)
+        worst = max(worst, st["max_ratio"])
+        assert st["bad"] == 0, (e, st["bad"], st["max_ratio"])
     print(f"[moe] grouped T={T} E={E} k={k} H={H} N={N} epi={epi} out={out_dtype}: experts checked {len(errs)}, "
-          f"max rel err {max(errs):.2e}", flush=True)
+          f"max rel err {max(errs):.2e}, element-wise max ratio to the bound {worst:.3f}", flush=True)
     return out, offsets
 
 
