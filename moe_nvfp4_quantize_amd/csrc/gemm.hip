@@ -807,7 +807,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     for (int i = 0; i < F; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa8[i], ob8[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob8[j], oa8[i], acc[i][j], 0, 0, 0);
   };
   // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), FM * FN
   // times; NV memory transfers and ND LDS reads spread evenly.  The reads of a
@@ -841,15 +841,24 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   };
 
   // ---------------------------------------------------------------- epilogue
-  // Each wave stages RPP rows of one fragment row i at a time in its own part
-  // of the code stage of the tile's last K step (free from the mid-step
-  // barrier of that step until the next step's transfers, which a workgroup
-  // barrier after the epilogue holds back), then writes them out 16 bytes per
-  // lane.  Accumulator register r of lane (l32, lh) in a 32x32 tile holds row
-  // 8*(r/4) + 4*lh + (r%4), column l32.
+  // The MFMAs take the weight fragment as their first operand, so accumulator
+  // register r = 4q + e of lane (l32, lh) in a 32x32 tile holds output row l32,
+  // column 8q + 4lh + e: each lane holds four runs of four consecutive columns
+  // of one row.  Each wave stages RPP rows of one fragment row i at a time in
+  // its own part of the code stage of the tile's last K step (free from the
+  // mid-step barrier of that step until the next step's transfers, which a
+  // workgroup barrier after the epilogue holds back), one 8-byte (bf16) or
+  // 16-byte (float) LDS store per run, then reads them back 16 bytes per lane
+  // and writes them out.  Staged rows are not padded (a fragment row of a
+  // 256 x 256 tile fills a stage): the 16-byte chunks of staged row t are
+  // rotated by t / (rows per 256 bytes), so that the rows of one store spread
+  // over the banks.
   constexpr int ROW_ELEMS = WN_OUT;
-  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT) + 16;  // +16: bank spread
-  constexpr int RPP = 4 * 16 * ROW_BYTES <= CODE_STAGE ? 16 : 8;  // rows per pass
+  constexpr int ROW_BYTES = ROW_ELEMS * (int)sizeof(OutT);
+  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per staged row
+  constexpr int RPP = 4 * 32 * ROW_BYTES <= CODE_STAGE ? 32 : (4 * 16 * ROW_BYTES <= CODE_STAGE ? 16 : 8);
+  constexpr int RW = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;  // staged rows per 256 bytes
+  static_assert(ROW_BYTES % 16 == 0, "whole 16-byte chunks per staged row");
   static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
   auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf) {
@@ -861,6 +870,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     const uint32_t el32 = ln % 32, elh = ln / 32;
     uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
     const uint32_t col0 = tn * BN_OUT + wn * WN_OUT;
+    // byte offset of 16-byte chunk c of staged row t
+    auto at = [&](uint32_t t, uint32_t c) { return t * ROW_BYTES + ((c + t / RW) % CPR) * 16; };
     // output value of accumulator register r of fragments (i, j) (with the
     // gate: of gate fragment j and its up fragment j + HALF)
     auto value = [&](int i, int j, int r) -> float {
@@ -873,24 +884,26 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       if ((uint32_t)i >= nf) break;  // rows past the tile's end: nothing to write
 #pragma unroll
       for (int ps = 0; ps < 32 / RPP; ++ps) {
-#pragma unroll
-        for (int r = ps * (RPP / 2); r < (ps + 1) * (RPP / 2); r += 2) {
-          // registers r and r + 1: rows tr and tr + 1 of the lane's column
-          __builtin_amdgcn_sched_barrier(0);
-          const uint32_t tr = 8 * (r / 4) + 4 * elh + (r % 4) - ps * RPP;
-          uint8_t *row = slab + tr * ROW_BYTES;
+        // the lanes whose row falls in this pass store their runs
+        if (el32 / RPP == (uint32_t)ps) {
+          const uint32_t t = el32 % RPP;
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
-            const float v0 = value(i, j, r), v1 = value(i, j, r + 1);
-            if constexpr (sizeof(OutT) == 2) {
-              // both rounded to nearest even by one packed convert
-              const float2v f = {v0, v1};
-              const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
-              reinterpret_cast<uint16_t *>(row)[j * 32 + el32] = (uint16_t)pk;
-              reinterpret_cast<uint16_t *>(row + ROW_BYTES)[j * 32 + el32] = (uint16_t)(pk >> 16);
-            } else {
-              reinterpret_cast<float *>(row)[j * 32 + el32] = v0;
-              reinterpret_cast<float *>(row + ROW_BYTES)[j * 32 + el32] = v1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              __builtin_amdgcn_sched_barrier(0);
+              const float v0 = value(i, j, 4 * q), v1 = value(i, j, 4 * q + 1);
+              const float v2 = value(i, j, 4 * q + 2), v3 = value(i, j, 4 * q + 3);
+              if constexpr (sizeof(OutT) == 2) {
+                // rounded to nearest even two at a time by the packed convert
+                const float2v f01 = {v0, v1}, f23 = {v2, v3};
+                const u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f01, bf16x2v)),
+                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, bf16x2v))};
+                *reinterpret_cast<u32x2 *>(slab + at(t, 4 * j + q) + elh * 8) = pk;
+              } else {
+                const u32x4 fv = {f2u(v0), f2u(v1), f2u(v2), f2u(v3)};
+                *reinterpret_cast<u32x4 *>(slab + at(t, 8 * j + 2 * q + elh)) = fv;
+              }
             }
           }
         }
@@ -900,39 +913,42 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         __builtin_amdgcn_wave_barrier();
         const uint32_t rbase = r0 + (NWM * i + wm) * 32 + ps * RPP;
         if constexpr (QOUT) {
-          // NVFP4 output with the static global scale: one 16-element block per
-          // lane (RPP rows x ROW_ELEMS / 16 blocks), the quantizer's arithmetic
-          static_assert(RPP * (ROW_ELEMS / 16) == 64, "one block per lane");
-          const uint32_t tr = ln / (ROW_ELEMS / 16), bk = ln % (ROW_ELEMS / 16);
-          const uint32_t row = rbase + tr, col = col0 + bk * 16;
-          if (row < row_end && col < n_out) {
-            const u32x4 *hv = reinterpret_cast<const u32x4 *>(slab + tr * ROW_BYTES + bk * 64);
-            float v[16];
+          // NVFP4 output with the static global scale: 16-element blocks (four
+          // staged chunks) one per lane at a time, the quantizer's arithmetic
+          constexpr int BPR = ROW_ELEMS / 16, NB = RPP * BPR;
+          static_assert(NB % 64 == 0, "whole rounds of blocks");
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const u32x4 t = hv[k];
+          for (int b0 = 0; b0 < NB; b0 += 64) {
+            const uint32_t b = b0 + ln, tr = b / BPR, bk = b % BPR;
+            const uint32_t row = rbase + tr, col = col0 + bk * 16;
+            if (row < row_end && col < n_out) {
+              float v[16];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[4 * k + e] = u2f(t[e]);  // (by value: a bit cast
-                                                                     // of a vector element
-                                                                     // lvalue reads element 0)
+              for (int k = 0; k < 4; ++k) {
+                const u32x4 tv = *reinterpret_cast<const u32x4 *>(slab + at(tr, bk * 4 + k));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * k + e] = u2f(tv[e]);  // (by value: a bit cast
+                                                                        // of a vector element
+                                                                        // lvalue reads element 0)
+              }
+              float bmax = 0.0f;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(v[e]));
+              const uint32_t sc = block_scale_code(bmax, h_six_g, h_inv_six_g);
+              const float rr = 1.0f / (e4m3_value(sc) * h_g);
+              uint32_t lo = 0, hi = 0;
+              lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0] * rr, v[1] * rr, 1.0f, 0);
+              lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2] * rr, v[3] * rr, 1.0f, 1);
+              lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4] * rr, v[5] * rr, 1.0f, 2);
+              lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6] * rr, v[7] * rr, 1.0f, 3);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8] * rr, v[9] * rr, 1.0f, 0);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10] * rr, v[11] * rr, 1.0f, 1);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12] * rr, v[13] * rr, 1.0f, 2);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14] * rr, v[15] * rr, 1.0f, 3);
+              *reinterpret_cast<uint64_t *>(p.h_q + (int64_t)row * (n_out / 2) + col / 2) =
+                  (uint64_t)lo | ((uint64_t)hi << 32);
+              p.h_s[(int64_t)row * (n_out / 16) + col / 16] = (uint8_t)sc;
             }
-            float bmax = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, fabsf(v[e]));
-            const uint32_t sc = block_scale_code(bmax, h_six_g, h_inv_six_g);
-            const float rr = 1.0f / (e4m3_value(sc) * h_g);
-            uint32_t lo = 0, hi = 0;
-            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0] * rr, v[1] * rr, 1.0f, 0);
-            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[2] * rr, v[3] * rr, 1.0f, 1);
-            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[4] * rr, v[5] * rr, 1.0f, 2);
-            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[6] * rr, v[7] * rr, 1.0f, 3);
-            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[8] * rr, v[9] * rr, 1.0f, 0);
-            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[10] * rr, v[11] * rr, 1.0f, 1);
-            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[12] * rr, v[13] * rr, 1.0f, 2);
-            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[14] * rr, v[15] * rr, 1.0f, 3);
-            *reinterpret_cast<uint64_t *>(p.h_q + (int64_t)row * (n_out / 2) + col / 2) =
-                (uint64_t)lo | ((uint64_t)hi << 32);
-            p.h_s[(int64_t)row * (n_out / 16) + col / 16] = (uint8_t)sc;
           }
           __builtin_amdgcn_wave_barrier();
           continue;
@@ -940,14 +956,13 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk:
         // every chunk of the pass is read from LDS first, then all are stored
         constexpr int VEC = 16 / (int)sizeof(OutT);
-        constexpr int CPR = ROW_ELEMS / VEC;  // chunks per row
         constexpr int NCH = RPP * CPR, NIT = (NCH + 63) / 64;
         u32x4 chunk[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const uint32_t c = ln + it * 64;
           if (NCH % 64 == 0 || c < (uint32_t)NCH)
-            chunk[it] = *reinterpret_cast<const u32x4 *>(slab + (c / CPR) * ROW_BYTES + (c % CPR) * 16);
+            chunk[it] = *reinterpret_cast<const u32x4 *>(slab + at(c / CPR, c % CPR));
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
