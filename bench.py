@@ -38,6 +38,8 @@ Prints ONE JSON line.
 """
 
 import argparse
+import contextlib
+import gc
 import ctypes
 import hashlib
 import json
@@ -156,24 +158,41 @@ class Timer:
         return {n: spread(self.durations(n)) for n in self.names}
 
 
+@contextlib.contextmanager
+def gc_paused():
+    """Python's collector paused (after a collection) while a timed loop runs:
+    a collection between the two events around a kernel would leave the GPU
+    idle inside the interval, waiting for the next launch."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
+
+
 def run_timed(step, n, first=0):
     """Mean ms of n steps (step(i)) with events around the whole run."""
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(first, first + n):
-        step(i)
-    b.record()
-    torch.cuda.synchronize()
+    with gc_paused():
+        a.record()
+        for i in range(first, first + n):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
     return a.elapsed_time(b) / n
 
 
 def run_kernels(step, names, n, first=0):
     """Per-kernel event durations over n steps (step(i, timer))."""
     tm = Timer(names)
-    for i in range(first, first + n):
-        step(i, tm)
-    torch.cuda.synchronize()
+    with gc_paused():
+        for i in range(first, first + n):
+            step(i, tm)
+        torch.cuda.synchronize()
     return tm.stats()
 
 
