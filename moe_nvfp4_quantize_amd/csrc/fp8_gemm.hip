@@ -27,9 +27,13 @@
 //    step.
 //  * Fragments are double buffered in registers: the LDS reads of step s + 1
 //    are issued first and complete behind the 16 MFMAs of step s, over which
-//    the transfers of step s + 4 are spread.
-//  * Tiles are ordered XCD-aware (dense_tile).  The epilogue stages each
-//    wave's 32-row slab through LDS so that global stores are 16 bytes per lane.
+//    the transfers of step s + 4 are spread.  (Spreading the reads over the
+//    MFMAs too, as the NVFP4 kernel does with its half-step reads, cost 6.5%:
+//    here they are a whole step ahead of their use.)
+//  * Tiles are ordered XCD-aware (dense_tile).  The MFMAs take the weight
+//    fragment first, so each lane holds runs of four output columns of one
+//    row; the epilogue stages each wave's 32-row slab through LDS with 8- or
+//    16-byte stores so that global stores are 16 bytes per lane.
 //  * K % 128 != 0 or row offsets beyond 32 bits take a plain kernel: direct
 //    16-byte global loads into registers, one 32 x 32 tile per wave.
 #include "nvfp4_common.hpp"
@@ -45,6 +49,9 @@ namespace {
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int KS = 64;  // K elements (bytes) per step
 
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_dma_kernel(Fp8GemmParams p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8(xa[C][i], xb[C][j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_fp8(xb[C][j], xa[C][i], acc[i][j]);
     // the transfers spread over the MFMAs, at most one after each
     constexpr int NM = FM * FN;
     static_assert(TN <= NM, "interleave shares");
@@ -185,40 +192,67 @@ __global__ __launch_bounds__(256, 1) void fp8_gemm_dma_kernel(Fp8GemmParams p) {
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
-  // Accumulator register r of lane (l32, lh) in a 32 x 32 tile holds row
-  // 8 (r / 4) + 4 lh + r % 4, column l32.  Each wave stages one fragment row
-  // (32 rows x 128 columns) at a time in its own part of LDS, then writes it
-  // out 16 bytes per lane.
+  // The MFMAs take the weight fragment first, so accumulator register
+  // r = 4q + e of lane (l32, lh) in a 32 x 32 tile holds output row l32, column
+  // 8q + 4lh + e: four runs of four consecutive columns of one row.  Each wave
+  // stages one fragment row (32 rows x 128 columns) at a time in its own part of
+  // LDS, one 8-byte (bf16) or 16-byte (float) store per run, the 16-byte chunks
+  // of staged row t rotated by t / (rows per 256 bytes) so that the rows of one
+  // store spread over the banks, then reads every chunk back and writes it out
+  // 16 bytes per lane.
   const float scale = (*p.a_g) * (*p.b_g);
-  constexpr int ROW_BYTES = WN * (int)sizeof(OutT) + 16;  // +16: bank spread
+  constexpr int ROW_BYTES = WN * (int)sizeof(OutT);
+  constexpr int CPR = ROW_BYTES / 16;  // 16-byte chunks per staged row
+  constexpr int RW = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
   static_assert(4 * 32 * ROW_BYTES <= NST * STAGE, "epilogue staging must fit");
   uint8_t *slab = smem + wave * 32 * ROW_BYTES;
+  auto at = [&](uint32_t t, uint32_t c) { return t * ROW_BYTES + ((c + t / RW) % CPR) * 16; };
   OutT *Cp = static_cast<OutT *>(p.c);
   const uint32_t ccol0 = col0 + wn * WN;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t tr = 8 * (r / 4) + 4 * lh + (r % 4);
-      OutT *dst = reinterpret_cast<OutT *>(slab + tr * ROW_BYTES);
+    for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) dst[j * 32 + l32] = to_out<OutT>(acc[i][j][r] * scale);
+      for (int q = 0; q < 4; ++q) {
+        const float v0 = acc[i][j][4 * q] * scale, v1 = acc[i][j][4 * q + 1] * scale;
+        const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
+        if constexpr (sizeof(OutT) == 2) {
+          // rounded to nearest even two at a time by the packed convert
+          const float2v f01 = {v0, v1}, f23 = {v2, v3};
+          const u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f01, bf16x2v)),
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, bf16x2v))};
+          *reinterpret_cast<u32x2 *>(slab + at(l32, 4 * j + q) + lh * 8) = pk;
+        } else {
+          const u32x4 fv = {f2u(v0), f2u(v1), f2u(v2), f2u(v3)};
+          *reinterpret_cast<u32x4 *>(slab + at(l32, 8 * j + 2 * q + lh)) = fv;
+        }
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    // the slab is this wave's own: ordering inside the wave suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     constexpr int VEC = 16 / (int)sizeof(OutT);
-    constexpr int CPR = WN / VEC;  // 16-byte chunks per row
+    constexpr int NCH = 32 * CPR, NIT = NCH / 64;
+    static_assert(NCH % 64 == 0, "whole rounds of chunks");
     const uint32_t rbase = row0 + wm * WM + i * 32;
-    for (int c = lane; c < 32 * CPR; c += 64) {
-      const uint32_t tr = c / CPR, cc = c % CPR;
-      const uint32_t row = rbase + tr, col = ccol0 + cc * VEC;
+    u32x4 chunk[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint32_t c = lane + it * 64;
+      chunk[it] = *reinterpret_cast<const u32x4 *>(slab + at(c / CPR, c % CPR));
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const uint32_t c = lane + it * 64;
+      const uint32_t row = rbase + c / CPR, col = ccol0 + (c % CPR) * VEC;
       if (row >= p.M) continue;
-      const uint8_t *srcp = slab + tr * ROW_BYTES + cc * 16;
       OutT *gp = Cp + (int64_t)row * p.ldc + col;
       if (VSTORE && col + VEC <= p.N) {
-        *reinterpret_cast<u32x4 *>(gp) = *reinterpret_cast<const u32x4 *>(srcp);
+        *reinterpret_cast<u32x4 *>(gp) = chunk[it];
       } else {
-        const OutT *sv = reinterpret_cast<const OutT *>(srcp);
+        OutT sv[VEC];
+        __builtin_memcpy(sv, &chunk[it], 16);
         for (int e = 0; e < VEC; ++e)
           if (col + e < p.N) gp[e] = sv[e];
       }

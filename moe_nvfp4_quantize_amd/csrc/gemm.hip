@@ -421,20 +421,23 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
          (n_out / bn_out) % 2 == 0;
 }
 
-// BM x 256 output tile (BM = 128, 192 or 256), four waves: 2 x 2 of BM/2 x 128
-// (BM/64 x 4 MFMA tiles each), or, for 128-row tiles and grouped 192-row
-// tiles, 1 x 4 of BM x 64 (BM/32 x 2 MFMA tiles each).
+// BM x BN output tile (BM = 128, 192 or 256; BN = 256, or 320 for dense
+// products of at most 128 rows), four waves: 2 x 2 of BM/2 x BN/2 (BM/64 x
+// BN/64 MFMA tiles each), or, for 128 x 256 tiles and grouped 192-row tiles,
+// 1 x 4 of BM x 64 (BM/32 x 2 MFMA tiles each).  The MFMAs take the weight
+// fragment first, so an accumulator holds runs of output columns of one row
+// (the epilogue below).
 //  * Codes and scales go from global memory straight into LDS
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
 //    LDS), so no registers hold staged data and no LDS store instructions run.
 //  * Codes: three stages of one K step (128 elements: 64 bytes per row),
-//    fetched two steps ahead (four stages, three steps ahead, for 128-row
+//    fetched two steps ahead (four stages, three steps ahead, for 128 x 256
 //    tiles).  Scales: two chunks of eight K steps (64 bytes per
 //    row), so that a transfer reads 64 contiguous bytes of a row instead of 8;
 //    the next chunk is fetched during the first four steps of the current one.
-//  * Each step issues the same number of transfers (BM/64 + 4 code, 2 scale;
-//    extra ones reload data that is not read any more, or rewrite identical
-//    bytes), so one wait count serves
+//  * Each step issues the same number of transfers ((BM + BN)/64 code, one A
+//    and one or two B scale transfers; extra ones reload data that is not read
+//    any more, or rewrite identical bytes), so one wait count serves
 //    every step: at the mid-step barrier only the step's own transfers may be
 //    in flight.  The transfers are spread over the step's MFMAs so that the
 //    memory pipeline never backs up the wave's in-order issue.
