@@ -447,6 +447,12 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
 //  * Decode is software pipelined: while the MFMAs of sub-step t run (16 for
 //    256-row tiles), the operands of sub-step t + 1 are decoded (one MFMA, then
 //    a few VALU instructions, in turn).
+// The fragments a wave multiplies in a tile: F of A (row groups) and FB of B.
+template <int F_, int FB_>
+struct Frags {
+  static constexpr int F = F_, FB = FB_;
+};
+
 template <int BM, bool GROUPED, bool SILU, bool VSTORE, typename OutT, bool QOUT = false, int NWM = 2,
           int BN = 256>
 __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
@@ -757,38 +763,38 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // fragments of half h of the code stage of global step g
-  // (helpers take F, the number of this wave's A fragments that hold rows of
-  // the tile: 32-row groups past the last row are not read, decoded or
-  // multiplied)
+  // (helpers take Frags<F, FB>: F, the number of this wave's A fragments that
+  // hold rows of the tile (32-row groups past the last row are not read,
+  // decoded or multiplied), and FB, the number of B fragments it multiplies)
   auto read_half = [&](auto f_tag, uint32_t g, int h, u32x4 *xa, u32x4 *xb) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
     const uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
 #pragma unroll
     for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
+    for (int j = 0; j < FB; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
   };
   // scale dword of K step ks held in global chunk gc: piece (ks % 8) / 2 of
   // the row's 64 bytes, half ks % 2
   auto read_scales = [&](auto f_tag, uint32_t gc, uint32_t ks, uint32_t *xa, uint32_t *xb) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
     const uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + (ks % 2) * 8;
     const uint32_t q = (ks % SC_STEPS) / 2;
 #pragma unroll
     for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) xb[j] = *reinterpret_cast<const uint32_t *>(st + rowSB[j] + ((q ^ swB[j]) * 16));
+    for (int j = 0; j < FB; ++j) xb[j] = *reinterpret_cast<const uint32_t *>(st + rowSB[j] + ((q ^ swB[j]) * 16));
   };
   // scale pairs of one step: block b of the lane's four is pair b % 2, element b / 2
   auto pairs = [&](auto f_tag, const uint32_t *ya, const uint32_t *yb, half2v (*pa)[2], half2v (*pb)[2]) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
       pa[i][0] = scale_pair(ya[i]);
       pa[i][1] = scale_pair(ya[i] >> 8);
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int j = 0; j < FB; ++j) {
       pb[j][0] = scale_pair(yb[j]);
       pb[j][1] = scale_pair(yb[j] >> 8);
     }
@@ -797,31 +803,31 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // half-t/4 fragments, block b = t / 2 of the lane's four
   auto decode_step = [&](auto f_tag, int t, const u32x4 *xa, const u32x4 *xb, half2v (*pa)[2],
                          half2v (*pb)[2], half8v *oa8, half8v *ob8) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
     const int b = t / 2;
 #pragma unroll
     for (int i = 0; i < F; ++i) oa8[i] = decode8(xa[i][t % 4], pa[i][b % 2][b / 2]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) ob8[j] = decode8(xb[j][t % 4], pb[j][b % 2][b / 2]);
+    for (int j = 0; j < FB; ++j) ob8[j] = decode8(xb[j][t % 4], pb[j][b % 2][b / 2]);
   };
   auto mfmas = [&](auto f_tag, const half8v *oa8, const half8v *ob8) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
 #pragma unroll
     for (int i = 0; i < F; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ob8[j], oa8[i], acc[i][j], 0, 0, 0);
   };
-  // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), FM * FN
+  // one MFMA, then VPM VALU (a sub-step's decode spread over its MFMAs), F * FB
   // times; NV memory transfers and ND LDS reads spread evenly.  The reads of a
   // half step's operands go between its first MFMAs: issued as one burst right
   // after a barrier, the four waves' reads queue behind each other and hold up
   // the MFMAs (2-3% of the prefill GEMM's time)
   auto interleave = [&](auto f_tag, auto nv_tag, auto nd_tag) {
-    constexpr int F = decltype(f_tag)::value;
-    constexpr int NV = decltype(nv_tag)::value, NM = F * FN;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
+    constexpr int NV = decltype(nv_tag)::value, NM = F * FB;
     constexpr int ND = decltype(nd_tag)::value;
-    constexpr int VPM = (8 * (F + FN) + NM - 1) / NM;
+    constexpr int VPM = (8 * (F + FB) + NM - 1) / NM;
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -864,7 +870,10 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   static_assert(ROW_BYTES % 16 == 0, "whole 16-byte chunks per staged row");
   static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
-  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf) {
+  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf, auto split_tag) {
+    // a column-split tile (split_tag true): one fragment row, row group 0 for
+    // both wave rows, wave row wm holding half of its wave column's outputs
+    constexpr bool SPL = decltype(split_tag)::value;
     // The lane's index, computed afresh here: lane-derived addresses kept live
     // across the K loop for the epilogue get spilled, and each reload waits for
     // every transfer in flight, including the next tile's first steps.
@@ -872,16 +881,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const uint32_t el32 = ln % 32, elh = ln / 32;
     uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
-    const uint32_t col0 = tn * BN_OUT + wn * WN_OUT;
+    const uint32_t col0 = tn * BN_OUT + wn * WN_OUT + (SPL ? wm * (WN_OUT / 2) : 0u);
     // byte offset of 16-byte chunk c of staged row t
     auto at = [&](uint32_t t, uint32_t c) { return t * ROW_BYTES + ((c + t / RW) % CPR) * 16; };
     // output value of accumulator register r of fragments (i, j) (with the
     // gate: of gate fragment j and its up fragment j + HALF)
+    constexpr int HOFF = SPL ? 1 : HALF;  // up fragment of gate fragment j: j + HOFF
     auto value = [&](int i, int j, int r) -> float {
-      if constexpr (SILU) return silu(acc[i][j][r] * out_scale) * (acc[i][j + HALF][r] * out_scale);
+      if constexpr (SILU) return silu(acc[i][j][r] * out_scale) * (acc[i][j + HOFF][r] * out_scale);
       else return acc[i][j][r] * out_scale;
     };
-    constexpr int NJ = SILU ? HALF : FN;
+    constexpr int NJ = SPL ? (SILU ? 1 : 2) : (SILU ? HALF : FN);
+    // 16-byte chunks of a staged row that hold outputs, and 16-element blocks
+    constexpr int CPR_E = SPL ? CPR / 2 : CPR, BPR_E = (SPL ? ROW_ELEMS / 2 : ROW_ELEMS) / 16;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if ((uint32_t)i >= nf) break;  // rows past the tile's end: nothing to write
@@ -914,17 +926,16 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         // workgroup-scope fence would also wait for every load in flight)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        const uint32_t rbase = r0 + (NWM * i + wm) * 32 + ps * RPP;
+        const uint32_t rbase = r0 + (SPL ? 0u : (NWM * i + wm)) * 32 + ps * RPP;
         if constexpr (QOUT) {
           // NVFP4 output with the static global scale: 16-element blocks (four
           // staged chunks) one per lane at a time, the quantizer's arithmetic
-          constexpr int BPR = ROW_ELEMS / 16, NB = RPP * BPR;
-          static_assert(NB % 64 == 0, "whole rounds of blocks");
+          constexpr int NB = RPP * BPR_E;
 #pragma unroll
           for (int b0 = 0; b0 < NB; b0 += 64) {
-            const uint32_t b = b0 + ln, tr = b / BPR, bk = b % BPR;
+            const uint32_t b = b0 + ln, tr = b / BPR_E, bk = b % BPR_E;
             const uint32_t row = rbase + tr, col = col0 + bk * 16;
-            if (row < row_end && col < n_out) {
+            if ((NB % 64 == 0 || b < (uint32_t)NB) && row < row_end && col < n_out) {
               float v[16];
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
@@ -959,18 +970,18 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         // RPP rows x ROW_ELEMS outputs, 16 bytes (VEC elements) per lane-chunk:
         // every chunk of the pass is read from LDS first, then all are stored
         constexpr int VEC = 16 / (int)sizeof(OutT);
-        constexpr int NCH = RPP * CPR, NIT = (NCH + 63) / 64;
+        constexpr int NCH = RPP * CPR_E, NIT = (NCH + 63) / 64;
         u32x4 chunk[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const uint32_t c = ln + it * 64;
           if (NCH % 64 == 0 || c < (uint32_t)NCH)
-            chunk[it] = *reinterpret_cast<const u32x4 *>(slab + at(c / CPR, c % CPR));
+            chunk[it] = *reinterpret_cast<const u32x4 *>(slab + at(c / CPR_E, c % CPR_E));
         }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const uint32_t c = ln + it * 64;
-          const uint32_t row = rbase + c / CPR, col = col0 + (c % CPR) * VEC;
+          const uint32_t row = rbase + c / CPR_E, col = col0 + (c % CPR_E) * VEC;
           if ((NCH % 64 != 0 && c >= (uint32_t)NCH) || row >= row_end) continue;
           OutT *gp = C + (int64_t)row * p.ldc + col;
           if (VSTORE && col + VEC <= n_out) {
@@ -1020,7 +1031,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     const uint32_t groups = (rows_in + 31) / 32;
     const uint32_t nf = groups > wm ? min((groups - wm + NWM - 1) / NWM, (uint32_t)FM) : 0u;
     auto run = [&](auto f_tag) {
-    constexpr int F = decltype(f_tag)::value;
+    constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
     const auto ft = f_tag;
     // the tile's first step: its data landed before the previous barrier
     // (fetched during the previous tile), or just above
@@ -1078,7 +1089,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
         if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, part % 4);
         if constexpr (F > 0) {
-          if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>(), std::integral_constant<int, F + FN>());
+          if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>(), std::integral_constant<int, F + FB>());
           if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
           if (t == 2) interleave(ft, std::integral_constant<int, ((3 * TN + 3) / 4 - (2 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
           if (t == 3) interleave(ft, std::integral_constant<int, ((4 * TN + 3) / 4 - (3 * TN + 3) / 4) + NSC>(), std::integral_constant<int, 0>());
@@ -1109,11 +1120,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < F; ++i) asm volatile("" : "+v"(fa[i]), "+v"(na[i]));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
+            for (int j = 0; j < FB; ++j) asm volatile("" : "+v"(fb[j]), "+v"(nb[j]));
             pairs(ft, na, nb, npa, npb);
             decode_step(ft, 0, fa, fb, npa, npb, av[0], bv[0]);
           }
-          if (t == 4) interleave(ft, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * (F + FN)>());
+          if (t == 4) interleave(ft, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * (F + FB)>());
           else interleave(ft, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
         }
       }
@@ -1123,27 +1134,77 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         spa[i][1] = npa[i][1];
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+      for (int j = 0; j < FB; ++j) {
         spb[j][0] = npb[j][0];
         spb[j][1] = npb[j][1];
       }
     }
     };
+    // A grouped tile holding a single 32-row group (an expert's last few rows)
+    // splits columns instead of rows between the two wave rows: both take row
+    // group 0, wave row wm half of its wave column's B fragments (without the
+    // gate fragments 2 wm and 2 wm + 1; with it gate fragment wm and its up
+    // fragment HALF + wm), so that wave row 1 does not idle at every barrier.
+    // The per-wave offsets are remapped for the tile and restored after it.
+    constexpr bool CAN_SPLIT = GROUPED && NWM == 2 && FN == 4;
+    const bool split = CAN_SPLIT && groups == 1;
+    uint32_t keep_a[2] = {0, 0}, keep_sa = 0, keep_b[2][2] = {{0, 0}, {0, 0}}, keep_sb[2] = {0, 0},
+             keep_swb[2] = {0, 0};
+    if constexpr (CAN_SPLIT) {
+      if (split) {
+        const uint32_t j0 = SILU ? wm : 2 * wm, j1 = SILU ? HALF + wm : 2 * wm + 1;
+        auto pick = [&](const uint32_t (&v)[FN], uint32_t j) { return j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3]; };
+        uint32_t ob0[FN], ob1[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          ob0[j] = offB[j][0];
+          ob1[j] = offB[j][1];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) keep_a[h] = offA[0][h];
+        keep_sa = rowSA[0];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          keep_b[j][0] = offB[j][0];
+          keep_b[j][1] = offB[j][1];
+          keep_sb[j] = rowSB[j];
+          keep_swb[j] = swB[j];
+        }
+        const uint32_t nsb0 = pick(rowSB, j0), nsb1 = pick(rowSB, j1), nsw0 = pick(swB, j0), nsw1 = pick(swB, j1);
+        offB[0][0] = pick(ob0, j0);
+        offB[0][1] = pick(ob1, j0);
+        offB[1][0] = pick(ob0, j1);
+        offB[1][1] = pick(ob1, j1);
+        rowSB[0] = nsb0;
+        rowSB[1] = nsb1;
+        swB[0] = nsw0;
+        swB[1] = nsw1;
+        // wave row 1's first fragment holds rows 32..63: 32 rows back (the
+        // swizzle (r / 4) % 4 is the same 32 rows apart)
+        if (wm == 1) {
+          offA[0][0] -= 32 * 64;
+          offA[0][1] -= 32 * 64;
+          rowSA[0] -= 32 * 64;
+        }
+      }
+    }
+
     // dispatch on F (uniform per wave; every variant runs the same barriers)
-    if (nf >= (uint32_t)FM) run(std::integral_constant<int, FM>());
-    else if (nf == 0) run(std::integral_constant<int, 0>());
-    else if (nf == 1) run(std::integral_constant<int, 1>());
+    if (CAN_SPLIT && split) run(Frags<1, 2>());
+    else if (nf >= (uint32_t)FM) run(Frags<FM, FN>());
+    else if (nf == 0) run(Frags<0, FN>());
+    else if (nf == 1) run(Frags<1, FN>());
     else if constexpr (FM > 2) {
-      if (nf == 2) run(std::integral_constant<int, 2>());
+      if (nf == 2) run(Frags<2, FN>());
       else if constexpr (FM > 3) {
-        if (nf == 3) run(std::integral_constant<int, 3>());
+        if (nf == 3) run(Frags<3, FN>());
         else if constexpr (FM > 4) {
-          if (nf == 4) run(std::integral_constant<int, 4>());
+          if (nf == 4) run(Frags<4, FN>());
           else if constexpr (FM > 5) {
-            if (nf == 5) run(std::integral_constant<int, 5>());
+            if (nf == 5) run(Frags<5, FN>());
             else if constexpr (FM > 6) {
-              if (nf == 6) run(std::integral_constant<int, 6>());
-              else if constexpr (FM > 7) run(std::integral_constant<int, 7>());
+              if (nf == 6) run(Frags<6, FN>());
+              else if constexpr (FM > 7) run(Frags<7, FN>());
             }
           }
         }
@@ -1152,7 +1213,23 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
 
     // the tile is done: the next tile's first steps are already in flight
     wait_lgkm0();
-    epilogue(g - 1, row0, tile_n, nf);
+    if (CAN_SPLIT && split) {
+      epilogue(g - 1, row0, tile_n, 1u, std::true_type());
+      if constexpr (CAN_SPLIT) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) offA[0][h] = keep_a[h];
+        rowSA[0] = keep_sa;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          offB[j][0] = keep_b[j][0];
+          offB[j][1] = keep_b[j][1];
+          rowSB[j] = keep_sb[j];
+          swB[j] = keep_swb[j];
+        }
+      }
+    } else {
+      epilogue(g - 1, row0, tile_n, nf, std::false_type());
+    }
     // every wave's staging reads done before the next step's transfers rewrite
     // the stage (no wait for the transfers in flight: they fill other stages)
     wait_lgkm0();
