@@ -73,21 +73,26 @@ struct Tile {
   static_assert(BM * 4 % NT == 0 && BN * 4 % NT == 0, "code chunks must split evenly");
 };
 
-// two E4M3FN scale bytes (bits 7..0 and 23..16 of w) -> f16 pair (exact)
+// two E4M3FN scale bytes (bits 7..0 and 23..16 of w) -> f16 pair of the
+// scales divided by 256 (exact): the bytes moved up by 7 bits are the f16
+// encodings of s / 2^8 (f16 exponent bias 15 against E4M3's 7; E4M3
+// subnormals land on f16 subnormals); decode8 applies the factor 2^8 in its
+// code conversion instead of a multiply here
 __device__ __forceinline__ half2v scale_pair(uint32_t w) {
-  const uint32_t bits = (w & 0x00FF00FFu) << 7;
-  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(half2v, bits) * k256;
+  return __builtin_bit_cast(half2v, (w & 0x00FF00FFu) << 7);
 }
 
 // 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times the
-// f16 block scale s -> 8 exact f16 products
+// block scale s, given as s / 256 (scale_pair) -> 8 exact f16 products: the
+// conversion multiplies the codes by its power-of-two scale operand exactly
+// (codes x 256 <= 1536), and code x s needs at most 6 significant bits
+// between 2^-10 and 2688, well inside f16
 __device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
   const half2v s2 = {s, s};
-  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
-  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
-  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
-  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
   return (half8v){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -427,9 +432,11 @@ __host__ __device__ inline bool grouped_walk(int bm, bool silu, uint32_t K, uint
 // 1 x 4 of BM x 64 (BM/32 x 2 MFMA tiles each).  The MFMAs take the weight
 // fragment first, so an accumulator holds runs of output columns of one row
 // (the epilogue below).
-//  * Codes and scales go from global memory straight into LDS
-//    (global_load_lds_dwordx4: 64 lanes x 16 bytes into 1 KB of consecutive
-//    LDS), so no registers hold staged data and no LDS store instructions run.
+//  * Codes and scales go from global memory straight into LDS (64 lanes x 16
+//    bytes into 1 KB of consecutive LDS per transfer: buffer_load_dwordx4 ...
+//    lds for the codes of dense tiles, whose buffer range ends at the
+//    matrix's last row, global_load_lds_dwordx4 otherwise), so no registers
+//    hold staged data and no LDS store instructions run.
 //  * Codes: three stages of one K step (128 elements: 64 bytes per row),
 //    fetched two steps ahead (four stages, three steps ahead, for 128 x 256
 //    tiles).  Scales: two chunks of eight K steps (64 bytes per
@@ -648,18 +655,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // Global -> LDS transfers.  One transfer moves 64 lanes x 16 bytes into 1 KB
   // of consecutive LDS: transfer j of an operand covers slots s = j * 256 + tid,
   // i.e. tile row s / 4, physical 16-byte piece s % 4, which holds logical
-  // piece (s % 4) ^ swz(row) = pc for every j.  A lane's byte offset is
-  // min(l + base, last): dense tiles keep the lane part l (row inside the
-  // tile) and add the tile's first row as a uniform base, clamped to the last
-  // row of the matrix (rows past the end are never stored); grouped tiles hold
-  // the full offset of the gathered row (base 0, no clamp).  Offsets fit 32
-  // bits (checked by the host).
+  // piece (s % 4) ^ swz(row) = pc for every j.  Dense tiles keep the lane
+  // part l of a byte offset (row inside the tile): their codes load through a
+  // buffer resource based at the tile's first row, whose range check drops
+  // rows past the end of the matrix, and their scales at min(l + base, last),
+  // clamped to the last row (rows past the end are never stored); grouped
+  // tiles hold the full offset of the gathered row (base 0, no clamp).
+  // Offsets fit 32 bits (checked by the host).
   const uint32_t pc = (tid % 4) ^ swz(tid / 4);
   // (vectors, not arrays: an index known only at run time becomes selects)
   typedef std::conditional_t<(TB > 4), u32x8, u32x4> BOffsets;
   u32x4 la = {0, 0, 0, 0}, lsa = {0, 0, 0, 0};
   BOffsets lb, lsb;
-  uint32_t last_a, last_b, last_sa, last_sb;
+  uint32_t last_sa, last_sb;
   if (!GROUPED) {
 #pragma unroll
     for (int j = 0; j < TA; ++j) {
@@ -671,9 +679,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       lb[j] = (j * 64 + tid / 4) * kbytes + pc * 16;
       lsb[j] = (j * 64 + tid / 4) * kscales + pc * 16;
     }
-    last_a = (p.M - 1) * kbytes + pc * 16;
     last_sa = (p.M - 1) * kscales + pc * 16;
-    last_b = (p.N - 1) * kbytes + pc * 16;
     last_sb = (p.N - 1) * kscales + pc * 16;
   } else {
     const int32_t a_fallback = sRow[0];  // the tile's first row always exists
@@ -691,43 +697,81 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       lb[j] = rb * kbytes + pc * 16;
       lsb[j] = rb * kscales + pc * 16;
     }
-    last_a = last_b = last_sa = last_sb = 0xFFFFFFFFu;
+    last_sa = last_sb = 0xFFFFFFFFu;
   }
   __syncthreads();  // every wave is done with the set-up tables
   // first A row and first B row of a tile as used in the offsets (grouped: A
   // rows are gathered in full, B rows are whole unless the workgroup walks)
   auto a_base = [&](uint32_t r0) { return GROUPED ? 0u : r0; };
   auto b_base = [&](uint32_t tn) { return GROUPED ? (gwalk ? tn * BN_OUT : 0u) : tn * BN; };
-  // code transfer q (0 .. TN - 1; A first) of K step ks of the tile at (ar, bc),
-  // into the stage of global step g
-  auto issue_code = [&](uint32_t g, uint32_t ks, uint32_t ar, uint32_t bc, int q) {
-    uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
-    if (q < TA) {
-      const uint32_t off = min(la[q] + ar * kbytes, last_a);
-      __builtin_amdgcn_global_load_lds((glb_void *)(p.a_q + ks * 64 + off), (lds_void *)(st + q * 4096 + wave * 1024), 16, 0, 0);
+  // Dense tiles load through buffer resources that start at the tile's first
+  // row and end at the matrix's last byte: a lane whose row lies past the end
+  // is out of range and reads nothing from memory (those rows are never
+  // stored), so the lane offsets are rows inside the tile, need no clamp, and
+  // the K offset is a scalar.  Grouped tiles keep the full per-lane offsets of
+  // their gathered rows.
+  typedef __amdgpu_buffer_rsrc_t Rsrc;
+  auto rsrc = [&](const uint8_t *base, uint32_t bytes) -> Rsrc {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+  };
+  // the code stream's fetch tile (dense: its resources; grouped: its first
+  // rows as used in the offsets) and the scale stream's target tile (its first
+  // rows as used in the offsets)
+  Rsrc rA = rsrc(p.a_q, 0), rB = rA;
+  uint32_t f_ar = 0, f_bc = 0, s_ar = 0, s_bc = 0;
+  auto set_fetch = [&](uint32_t r0, uint32_t tn) {
+    if constexpr (!GROUPED) {
+      // (the second half of a split tile can start past the last row: empty)
+      rA = rsrc(p.a_q + (size_t)r0 * kbytes, p.M > r0 ? (p.M - r0) * kbytes : 0u);
+      rB = rsrc(bq + (size_t)tn * BN * kbytes, p.N > tn * BN ? (p.N - tn * BN) * kbytes : 0u);
     } else {
-      const uint32_t off = min(lb[q - TA] + bc * kbytes, last_b);
-      __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + off), (lds_void *)(st + CODE_B + (q - TA) * 4096 + wave * 1024), 16, 0, 0);
+      f_ar = a_base(r0);
+      f_bc = b_base(tn);
     }
   };
-  // scale transfers of part q (0..3) of chunk c of the tile at (ar, bc), into
-  // the buffer of global chunk gc: A transfer q % TA and B transfers q, q + 4,
-  // ... (the last one repeated past TB; q possibly not known at compile time:
-  // vector selects, no indexing into memory).  A piece past the end of the row
-  // reloads the chunk's first piece instead (K % 256 == 0 keeps that in the row).
-  auto issue_scales = [&](uint32_t gc, uint32_t c, uint32_t ar, uint32_t bc, uint32_t q) {
-    uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + wave * 1024;
-    const uint32_t back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16;
+  auto set_scale_target = [&](uint32_t r0, uint32_t tn) {
+    s_ar = a_base(r0);
+    s_bc = b_base(tn);
+  };
+  // code transfer q (0 .. TN - 1; A first) of K step ks of the fetch tile,
+  // into the stage at byte offset st
+  auto issue_code = [&](uint32_t st, uint32_t ks, int q) {
+    lds_void *dst = (lds_void *)(smem + st + (q < TA ? q * 4096 : CODE_B + (q - TA) * 4096) + wave * 1024);
+    if constexpr (!GROUPED) {
+      // (plain int operands: vector elements passed straight to the builtin
+      // make the host compilation drop the kernel's launch stub)
+      if (q < TA) __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, dst, 16, (int)(uint32_t)la[q], (int)(ks * 64), 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, dst, 16, (int)(uint32_t)lb[q - TA], (int)(ks * 64), 0, 0);
+    } else {
+      if (q < TA) __builtin_amdgcn_global_load_lds((glb_void *)(p.a_q + ks * 64 + la[q] + f_ar * kbytes), dst, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds((glb_void *)(bq + ks * 64 + lb[q - TA] + f_bc * kbytes), dst, 16, 0, 0);
+    }
+  };
+  // Scale transfers of part q (0..3) of chunk s_c of the target tile, into the
+  // buffer at s_buf: A transfer q % TA and B transfers q, q + 4, ... (the last
+  // one repeated past TB; q is not known at compile time).  A piece past the
+  // end of the row reloads the chunk's first piece instead.  Dense tiles:
+  // transfer j's rows lie 64 j rows past the first transfer's, clamped to the
+  // last row of the matrix.
+  uint32_t s_c = 0, s_buf = 0, back = 0;
+  auto issue_scales = [&](uint32_t q) {
+    uint8_t *st = smem + OFF_SC + s_buf + wave * 1024;
     const uint32_t ja = q % TA;
-    const uint32_t oa = min(lsa[ja] + ar * kscales, last_sa);
-    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + c * 64 + oa - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
+    uint32_t oa;
+    if constexpr (!GROUPED) oa = min(lsa[0] + (ja * 64 + s_ar) * kscales, last_sa);
+    else oa = lsa[ja];
+    __builtin_amdgcn_global_load_lds((glb_void *)(p.a_s + s_c * 64 + oa - back), (lds_void *)(st + ja * 4096), 16, 0, 0);
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       const uint32_t jb = min(q + 4 * sb, (uint32_t)TB - 1);
-      const uint32_t ob = min(lsb[jb] + bc * kscales, last_sb);
-      __builtin_amdgcn_global_load_lds((glb_void *)(bs + c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
+      uint32_t ob;
+      if constexpr (!GROUPED) ob = min(lsb[0] + (jb * 64 + s_bc) * kscales, last_sb);
+      else ob = lsb[jb] + s_bc * kscales;
+      __builtin_amdgcn_global_load_lds((glb_void *)(bs + s_c * 64 + ob - back), (lds_void *)(st + SC_B + jb * 4096), 16, 0, 0);
     }
   };
+  // the lanes' step back for chunk c (a piece past the row's end: its first piece)
+  auto scale_bases = [&](uint32_t c) { back = (c * 64 + pc * 16 < kscales) ? 0u : pc * 16; };
 
   const uint32_t wm = wave / NWN, wn = wave % NWN;
   const uint32_t l32 = lane % 32, lh = lane / 32;
@@ -766,19 +810,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // (helpers take Frags<F, FB>: F, the number of this wave's A fragments that
   // hold rows of the tile (32-row groups past the last row are not read,
   // decoded or multiplied), and FB, the number of B fragments it multiplies)
-  auto read_half = [&](auto f_tag, uint32_t g, int h, u32x4 *xa, u32x4 *xb) {
+  auto read_half = [&](auto f_tag, uint32_t stg, int h, u32x4 *xa, u32x4 *xb) {
     constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
-    const uint8_t *st = smem + (g % NSTAGE) * CODE_STAGE;
+    const uint8_t *st = smem + stg;
 #pragma unroll
     for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const u32x4 *>(st + offA[i][h]);
 #pragma unroll
     for (int j = 0; j < FB; ++j) xb[j] = *reinterpret_cast<const u32x4 *>(st + offB[j][h]);
   };
-  // scale dword of K step ks held in global chunk gc: piece (ks % 8) / 2 of
+  // scale dword of K step ks held in the chunk buffer at byte offset buf: piece (ks % 8) / 2 of
   // the row's 64 bytes, half ks % 2
-  auto read_scales = [&](auto f_tag, uint32_t gc, uint32_t ks, uint32_t *xa, uint32_t *xb) {
+  auto read_scales = [&](auto f_tag, uint32_t buf, uint32_t ks, uint32_t *xa, uint32_t *xb) {
     constexpr int F = decltype(f_tag)::F, FB = decltype(f_tag)::FB;
-    const uint8_t *st = smem + OFF_SC + (gc % 2) * SC_CHUNK + (ks % 2) * 8;
+    const uint8_t *st = smem + OFF_SC + buf + (ks % 2) * 8;
     const uint32_t q = (ks % SC_STEPS) / 2;
 #pragma unroll
     for (int i = 0; i < F; ++i) xa[i] = *reinterpret_cast<const uint32_t *>(st + rowSA[i] + ((q ^ swA[i]) * 16));
@@ -870,7 +914,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   static_assert(ROW_BYTES % 16 == 0, "whole 16-byte chunks per staged row");
   static_assert(4 * RPP * ROW_BYTES <= CODE_STAGE, "epilogue staging must fit a stage");
   OutT *C = static_cast<OutT *>(p.c);
-  auto epilogue = [&](uint32_t g, uint32_t r0, uint32_t tn, uint32_t nf, auto split_tag) {
+  auto epilogue = [&](uint32_t stg, uint32_t r0, uint32_t tn, uint32_t nf, auto split_tag) {
     // a column-split tile (split_tag true): one fragment row, row group 0 for
     // both wave rows, wave row wm holding half of its wave column's outputs
     constexpr bool SPL = decltype(split_tag)::value;
@@ -880,7 +924,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     uint32_t ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const uint32_t el32 = ln % 32, elh = ln / 32;
-    uint8_t *slab = smem + (g % NSTAGE) * CODE_STAGE + wave * RPP * ROW_BYTES;
+    uint8_t *slab = smem + stg + wave * RPP * ROW_BYTES;
     const uint32_t col0 = tn * BN_OUT + wn * WN_OUT + (SPL ? wm * (WN_OUT / 2) : 0u);
     // byte offset of 16-byte chunk c of staged row t
     auto at = [&](uint32_t t, uint32_t c) { return t * ROW_BYTES + ((c + t / RW) % CPR) * 16; };
@@ -1007,24 +1051,35 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
   // steps); scale chunk c + 1 (or the next tile's chunk 0) during the first
   // four steps of chunk c.  Every step issues TN + NSC transfers (near the end
   // the last step's codes again, into a stage nobody reads any more; outside
-  // the first four steps of a chunk the current chunk's scales again,
+  // the first four steps of a chunk the next chunk's scales again,
   // rewriting identical bytes), so at the mid-step barrier one wait count
   // leaves in flight only what was issued after the fetch of the next step.  At the last step of a
   // tile its epilogue runs, behind the already issued transfers of the next.
   uint32_t nrow0 = row0, nrow_end = row_end, ntile_n = tile_n;  // the tile after the current one
   if (my_tiles > 1) origin(1, &nrow0, &nrow_end, &ntile_n);
+  // scale stream: chunk 0 of the first tile into buffer 0
+  set_scale_target(row0, tile_n);
+  scale_bases(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) issue_scales(0, 0, a_base(row0), b_base(tile_n), j);
-  // steps 0 .. AHEAD - 1 (a short single tile reloads its last step into the
-  // stages past it, which nobody reads; a walk of several tiles has at least 8
-  // steps per tile)
+  for (int j = 0; j < 4; ++j) issue_scales(j);
+  // code stream: steps 0 .. AHEAD - 1 of the first tile into stages 0 ..
+  // AHEAD - 1 (a short single tile reloads its last step into the stages past
+  // it, which nobody reads; a walk of several tiles has at least 8 steps per
+  // tile, so the stream runs at most into the next tile)
+  set_fetch(row0, tile_n);
 #pragma unroll
   for (int st = 0; st < AHEAD; ++st)
 #pragma unroll
-    for (int q = 0; q < TN; ++q)
-      issue_code(st, min((uint32_t)st, nsteps - 1), a_base(row0), b_base(tile_n), q);
+    for (int q = 0; q < TN; ++q) issue_code(st * CODE_STAGE, min((uint32_t)st, nsteps - 1), q);
   wait_vm<(AHEAD - 1) * TN>();
-  uint32_t g = 0;
+  // byte offsets of the code stages of global steps g - 1 (the stage the
+  // fetch of step g + AHEAD fills), g, g + 1, ...: rotated after every step
+  uint32_t sp[NSTAGE];
+  sp[0] = (NSTAGE - 1) * CODE_STAGE;
+#pragma unroll
+  for (int k = 1; k < NSTAGE; ++k) sp[k] = (k - 1) * CODE_STAGE;
+  uint32_t f_ks = AHEAD;  // the K step of the fetch tile the code stream fetches next
+  uint32_t r_buf = 0;     // the scale buffer of the current step's chunk
   for (uint32_t ti = 0; ti < my_tiles; ++ti) {
     // this wave's A fragments that hold rows of the tile
     const uint32_t rows_in = min(row_end - min(row0, row_end), (uint32_t)BM);
@@ -1040,8 +1095,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     u32x4 fa[FM], fb[FN];
     uint32_t sa[FM], sb[FN];
     if constexpr (F > 0) {
-      read_half(ft, g, 0, fa, fb);
-      read_scales(ft, ti * cpt, 0, sa, sb);
+      read_half(ft, sp[1], 0, fa, fb);
+      read_scales(ft, r_buf, 0, sa, sb);
     }
     wait_lgkm0();
     half2v spa[FM][2], spb[FN][2];
@@ -1050,34 +1105,39 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       pairs(ft, sa, sb, spa, spb);
       decode_step(ft, 0, fa, fb, spa, spb, av[0], bv[0]);
     }
-    for (uint32_t ks = 0; ks < nsteps; ++ks, ++g) {
-      // codes of global step g + AHEAD
-      uint32_t fks = ks + AHEAD, far_ = a_base(row0), fbc = b_base(tile_n);
-      if (fks >= nsteps) {
+    for (uint32_t ks = 0; ks < nsteps; ++ks) {
+      // the code stream past its tile's end: the next tile (which becomes the
+      // fetch tile) or, after the last tile, that tile's last step again
+      if (f_ks >= nsteps) {
         if (ti + 1 < my_tiles) {
-          fks -= nsteps;
-          far_ = a_base(nrow0);
-          fbc = b_base(ntile_n);
+          f_ks -= nsteps;
+          set_fetch(nrow0, ntile_n);
         } else {
-          fks = nsteps - 1;
+          f_ks = nsteps - 1;
         }
       }
-      // scale chunk: the next one during the first four steps of a chunk
-      const uint32_t part = ks % SC_STEPS, chunk = ks / SC_STEPS, gchunk = ti * cpt + chunk;
-      uint32_t sc_g = gchunk, sc_c = chunk, sar = a_base(row0), sbc = b_base(tile_n);
-      if (part < 4) {
+      // the scale stream, at a chunk's first step: the next chunk (of this
+      // tile, or the next tile's first) into the other buffer, for all eight
+      // steps of the chunk (the last four rewrite identical bytes), or, after
+      // the last chunk of the last tile, this chunk again
+      const uint32_t part = ks % SC_STEPS;
+      if (part == 0) {
+        const uint32_t chunk = ks / SC_STEPS;
         if (chunk + 1 < cpt) {
-          sc_g = gchunk + 1;
-          sc_c = chunk + 1;
+          s_c = chunk + 1;
+          s_buf = r_buf ^ SC_CHUNK;
         } else if (ti + 1 < my_tiles) {
-          sc_g = gchunk + 1;
-          sc_c = 0;
-          sar = a_base(nrow0);
-          sbc = b_base(ntile_n);
+          s_c = 0;
+          s_buf = r_buf ^ SC_CHUNK;
+          set_scale_target(nrow0, ntile_n);
+        } else {
+          s_c = chunk;
+          s_buf = r_buf;
         }
+        scale_bases(s_c);
       }
       u32x4 ha[FM], hb[FN];
-      if constexpr (F > 0) read_half(ft, g, 1, ha, hb);
+      if constexpr (F > 0) read_half(ft, sp[1], 1, ha, hb);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         if constexpr (F > 0) {
@@ -1086,8 +1146,8 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
           else decode_step(ft, 4, ha, hb, spa, spb, av[0], bv[0]);
         }
 #pragma unroll
-        for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(g + AHEAD, fks, far_, fbc, q);
-        if (t == 3) issue_scales(sc_g, sc_c, sar, sbc, part % 4);
+        for (int q = (t * TN + 3) / 4; q < ((t + 1) * TN + 3) / 4; ++q) issue_code(sp[0], f_ks, q);
+        if (t == 3) issue_scales(part % 4);
         if constexpr (F > 0) {
           if (t == 0) interleave(ft, std::integral_constant<int, ((1 * TN + 3) / 4 - (0 * TN + 3) / 4)>(), std::integral_constant<int, F + FB>());
           if (t == 1) interleave(ft, std::integral_constant<int, ((2 * TN + 3) / 4 - (1 * TN + 3) / 4)>(), std::integral_constant<int, 0>());
@@ -1103,10 +1163,11 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
       asm volatile("" ::: "memory");
       // the next step's first half (at a tile's last step: not used)
       const uint32_t nks = ks + 1 < nsteps ? ks + 1 : 0;
+      const uint32_t nbuf = nks % SC_STEPS == 0 ? r_buf ^ SC_CHUNK : r_buf;  // a new chunk: the other buffer
       uint32_t na[FM], nb[FN];
       if constexpr (F > 0) {
-        read_half(ft, g + 1, 0, fa, fb);
-        read_scales(ft, ti * cpt + nks / SC_STEPS, nks, na, nb);
+        read_half(ft, sp[2], 0, fa, fb);
+        read_scales(ft, nbuf, nks, na, nb);
       }
       half2v npa[FM][2], npb[FN][2];
       if constexpr (F > 0) {
@@ -1138,6 +1199,12 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         spb[j][0] = npb[j][0];
         spb[j][1] = npb[j][1];
       }
+      const uint32_t s0 = sp[0];
+#pragma unroll
+      for (int k = 0; k + 1 < NSTAGE; ++k) sp[k] = sp[k + 1];
+      sp[NSTAGE - 1] = s0;
+      r_buf = nbuf;
+      ++f_ks;
     }
     };
     // A grouped tile holding a single 32-row group (an expert's last few rows)
@@ -1214,7 +1281,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
     // the tile is done: the next tile's first steps are already in flight
     wait_lgkm0();
     if (CAN_SPLIT && split) {
-      epilogue(g - 1, row0, tile_n, 1u, std::true_type());
+      epilogue(sp[0], row0, tile_n, 1u, std::true_type());
       if constexpr (CAN_SPLIT) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) offA[0][h] = keep_a[h];
@@ -1228,7 +1295,7 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
         }
       }
     } else {
-      epilogue(g - 1, row0, tile_n, nf, std::false_type());
+      epilogue(sp[0], row0, tile_n, nf, std::false_type());
     }
     // every wave's staging reads done before the next step's transfers rewrite
     // the stage (no wait for the transfers in flight: they fill other stages)
