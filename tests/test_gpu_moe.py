@@ -231,6 +231,19 @@ def test_grouped_gemm_without_gather(B):
     _grouped_case(B, 300, 6, 2, 256, 128, 0, seed=3, gather=False)
 
 
+# Rows read in place (no gather), no gate, as the layer's down projection
+# runs: K of 4, 5, 6, 8, 12 and 16 steps of 128, every tile height, experts left
+# empty by the skewed routing (E = 64 with k = 1), bf16 and float32 output;
+# every expert checked.
+@pytest.mark.parametrize("T,E,k,H,N,out", [(2048, 16, 1, 512, 1024, "bf16"), (800, 8, 2, 640, 512, "f32"),
+                                           (4096, 16, 1, 768, 2048, "bf16"), (2560, 16, 1, 1024, 1024, "f32"),
+                                           (960, 16, 1, 1536, 512, "bf16"), (1000, 64, 1, 2048, 768, "f32"),
+                                           (3000, 5, 3, 768, 256, "bf16"), (50, 3, 2, 1024, 4096, "f32")])
+def test_grouped_gemm_rows_in_place(B, T, E, k, H, N, out):
+    _grouped_case(B, T, E, k, H, N, 0, seed=T + E + H, gather=False,
+                  out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+
+
 @pytest.mark.parametrize("H,I", [(256, 128), (2048, 768)])
 def test_silu_gate_large_gate_values(B, H, I):
     """Gate values of several hundred in magnitude: below z = -88.7 the power of
