@@ -1022,6 +1022,19 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmParams p) {
           if (NCH % 64 == 0 || c < (uint32_t)NCH)
             chunk[it] = *reinterpret_cast<const u32x4 *>(slab + at(c / CPR_E, c % CPR_E));
         }
+        // every row of the pass exists and every chunk is whole (interior
+        // tiles): plain 16-byte stores at a per-lane base, no per-chunk checks
+        if (VSTORE && rbase + RPP <= row_end && col0 + CPR_E * VEC <= n_out) {
+          OutT *gb = C + (int64_t)rbase * p.ldc + col0;
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const uint32_t c = ln + it * 64;
+            if (NCH % 64 == 0 || c < (uint32_t)NCH)
+              *reinterpret_cast<u32x4 *>(gb + (int64_t)(c / CPR_E) * p.ldc + (c % CPR_E) * VEC) = chunk[it];
+          }
+          __builtin_amdgcn_wave_barrier();
+          continue;
+        }
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const uint32_t c = ln + it * 64;
