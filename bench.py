@@ -783,6 +783,7 @@ def main():
     # the other workloads first (each set up, measured and released in turn)
     configs = {}
     for name in others:
+        print(f"bench: {name}", file=sys.stderr, flush=True)
         st, rep = measure(B, name, steps=iters, warmup=max(10, args.warmup), kernel_iters=iters)
         configs[name] = rep
         del st
@@ -790,6 +791,7 @@ def main():
 
     # headline: W warm-up steps, exactly K timed steps, then the per-kernel pass
     kind = W.WORKLOADS[head]["kind"]
+    print(f"bench: {head} (headline)", file=sys.stderr, flush=True)
     st, rep = measure(B, head, steps=args.steps, warmup=args.warmup, kernel_iters=max(args.steps, iters),
                       static=args.static_scales)
     extra = {}
@@ -813,6 +815,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        print("bench: oracle baselines on the host", file=sys.stderr, flush=True)
         base = cpu_baselines([head] + others)
         cpu = base[head]
         for name in others:
