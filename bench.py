@@ -379,6 +379,36 @@ def ceilings(st, iters):
     return out
 
 
+def mfma_ceiling(iters=2000):
+    """Matrix-core rate of the ceiling kernel (one workgroup of four waves per
+    compute unit, each wave 128 x 128 of v_mfma_f32_32x32x16_f16 on register
+    operands): MFMAs alone, and with the GEMM's exact FP4 decode of the next
+    operands interleaved; median of 3 runs of 10 back-to-back launches."""
+    path = os.path.join(ROOT, "moe_nvfp4_quantize_amd", "libnvfp4_ceiling.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.ceiling_grid.restype = ctypes.c_uint32
+    lib.ceiling_grid.argtypes = [ctypes.c_uint32]
+    lib.ceiling_mfma.restype = ctypes.c_int
+    lib.ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    grid = lib.ceiling_grid(1)
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flops = grid * 4 * iters * 2 * 16 * (2 * 32 * 32 * 16)
+    out = {}
+    for label, dec in (("mfma_only", 0), ("mfma_with_decode", 1)):
+        if lib.ceiling_mfma(sink.data_ptr(), iters, dec, stream()) != 0:
+            return None
+        ms = statistics.median([run_timed(lambda i: lib.ceiling_mfma(sink.data_ptr(), iters, dec, stream()), 10)
+                                for _ in range(3)])
+        tf = flops / (ms * 1e-3) / 1e12
+        out[label] = dict(tflops=tf, frac_f16_peak=tf / F16_MFMA_PEAK_TFLOPS, ms=ms)
+    out["note"] = ("f16 MFMA 32x32x16 with f32 accumulation, no memory or LDS traffic; the clock the chip "
+                   "holds under this load sets it below the 2.5 PFLOP/s specification")
+    return out
+
+
 # ------------------------------------------------------------------- MoE
 
 
@@ -799,6 +829,7 @@ def main():
         extra.update(quantizer_legs(B, st, iters))
         ceil = ceilings(st, iters)
         extra["ceilings"] = ceil
+        extra["mfma_ceiling"] = mfma_ceiling()
         if ceil:
             for key in ("quantize_cold", "quantize_static_cold"):
                 extra[key]["frac_read_write_ceiling"] = extra[key]["gbs"] / ceil["read_write"]["gbs"]

@@ -15,10 +15,20 @@
 // Both walk the units grid-stride, consecutive threads on consecutive units,
 // UPT units per thread in flight; the host picks one workgroup per compute
 // unit or more.
+//
+// And the matrix-core ceiling of the GEMM's arithmetic, with no memory or LDS
+// traffic: one workgroup of four waves per compute unit, each wave a 128 x 128
+// block of 4 x 4 accumulators of v_mfma_f32_32x32x16_f16 on operands held in
+// registers (the GEMM's wave tile), either MFMAs alone or with the GEMM's exact
+// FP4 -> f16 decode of the next sub-step's operands (4 converts and 4 packed
+// multiplies per 8 codes, 8 fragments per 16 MFMAs) interleaved between them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 
 namespace {
 
@@ -88,9 +98,92 @@ uint32_t cu_count() {
   return n > 0 ? (uint32_t)n : 0u;
 }
 
+// 8 codes of a dword times a block scale (s / 256, as the GEMM keeps it) -> 8 f16
+__device__ __forceinline__ half8v decode8(uint32_t w, _Float16 s) {
+  const half2v s2 = {s, s};
+  const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+  const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+  const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+  const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+  return (half8v){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// iters x 2 sub-steps of 16 MFMAs per wave; DECODE: the operands of the next
+// sub-step decoded from codes that change every iteration (a scalar salt) while
+// the current sub-step's MFMAs run, one MFMA then a few VALU instructions in turn
+template <bool DECODE>
+__global__ __launch_bounds__(256, 1) void mfma_kernel(float *__restrict__ sink, uint32_t iters) {
+  constexpr int F = 4, NM = F * F, VPM = (9 * 2 * F + NM - 1) / NM;
+  float16v acc[F][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const _Float16 sc = (_Float16)0.00390625f;
+  uint32_t ca[F], cb[F];
+  half8v av[2][F], bv[2][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i) {
+    ca[i] = (threadIdx.x * 2654435761u) ^ (0x9e3779b9u * (i + 1));
+    cb[i] = (threadIdx.x * 2246822519u) ^ (0x85ebca6bu * (i + 1));
+    av[0][i] = av[1][i] = decode8(ca[i], sc);
+    bv[0][i] = bv[1][i] = decode8(cb[i], sc);
+  }
+  for (uint32_t it = 0; it < iters; ++it) {
+    const uint32_t salt = __builtin_amdgcn_readfirstlane(it * 0x01010101u);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[t][j], av[t][i], acc[i][j], 0, 0, 0);
+      if constexpr (DECODE) {
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+          av[t ^ 1][i] = decode8(ca[i] ^ salt ^ t, sc);
+          bv[t ^ 1][i] = decode8(cb[i] ^ salt ^ t, sc);
+        }
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  sink[blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
+
+uint32_t ceiling_grid(uint32_t wgs_per_cu);
+
+// Matrix-core ceiling: ceiling_grid(1) workgroups of 256 threads, each wave
+// 2 x iters x 16 MFMAs of 32 x 32 x 16 (f16 in, f32 accumulate), with or
+// without the exact FP4 decode in between; sink receives ceiling_grid(1) x 256
+// floats.  Returns a hipError_t.
+int ceiling_mfma(float *sink, uint32_t iters, int decode, hipStream_t stream) {
+  const uint32_t grid = ceiling_grid(1);
+  if (!sink || grid == 0 || iters == 0) return (int)hipErrorInvalidValue;
+  if (decode)
+    mfma_kernel<true><<<grid, 256, 0, stream>>>(sink, iters);
+  else
+    mfma_kernel<false><<<grid, 256, 0, stream>>>(sink, iters);
+  return (int)hipGetLastError();
+}
 
 // Workgroups the kernels below launch: wgs_per_cu per compute unit.
 uint32_t ceiling_grid(uint32_t wgs_per_cu) { return cu_count() * wgs_per_cu; }
