@@ -163,6 +163,15 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True, out_dty
     offsets = _np(r["offsets"]).astype(np.int64)
     src = _np(r["src_row"]) if gather else np.arange(R)
     experts = range(E) if sample is None else sample
+    _check_grouped(B, a, w, out, offsets, src, experts, epi, out_dtype,
+                   f"T={T} E={E} k={k} H={H} N={N} epi={epi} out={out_dtype}")
+    return out, offsets
+
+
+def _check_grouped(B, a, w, out, offsets, src, experts, epi, out_dtype, label):
+    """Every listed expert's rows of a grouped GEMM's output against the oracle:
+    relative Frobenius error at most TOL, and every element within the float32
+    accumulation bound."""
     a_np = (_np(a[0]), _np(a[1]), np.float32(a[2][0].item()))
     errs, worst = [], 0.0
     for e in experts:
@@ -187,9 +196,9 @@ def _grouped_case(B, T, E, k, H, N, epi, seed, sample=None, gather=True, out_dty
         st = check(a_e, b_e, got, out_dtype == torch.bfloat16)
         worst = max(worst, st["max_ratio"])
         assert st["bad"] == 0, (e, st["bad"], st["max_ratio"])
-    print(f"[moe] grouped T={T} E={E} k={k} H={H} N={N} epi={epi} out={out_dtype}: experts checked {len(errs)}, "
+    assert errs, "no expert had rows"
+    print(f"[moe] grouped {label}: experts checked {len(errs)}, "
           f"max rel err {max(errs):.2e}, element-wise max ratio to the bound {worst:.3f}", flush=True)
-    return out, offsets
 
 
 # Rows per expert decide the grouped kernel's tile height (128, 192 or 256
@@ -242,6 +251,70 @@ def test_grouped_gemm_without_gather(B):
 def test_grouped_gemm_rows_in_place(B, T, E, k, H, N, out):
     _grouped_case(B, T, E, k, H, N, 0, seed=T + E + H, gather=False,
                   out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+
+
+# Many experts: the kernel's expert scan gives each of its 256 threads
+# ceil(E / 256) experts, so E = 1000 (routed, about 2.4 rows per expert), 3000
+# and 65536 (the ABI's maximum) take 4, 12 and 256 experts per thread.  The
+# last two build the segment offsets directly: most experts empty, a few with
+# one to several whole tiles, rows read through an arbitrary gather list.
+@pytest.mark.parametrize("epi", [0, 1])
+def test_grouped_gemm_many_experts_routed(B, epi):
+    _grouped_case(B, 600, 1000, 4, 256, 128, epi, seed=1000 + epi)
+
+
+@pytest.mark.parametrize("E,epi,out", [(3000, 0, "f32"), (3000, 1, "bf16"), (65536, 0, "bf16")])
+def test_grouped_gemm_many_experts_offsets(B, E, epi, out):
+    dev = "cuda"
+    H, N = 256, 128
+    rng = np.random.default_rng(E + epi)
+    counts = np.zeros(E, dtype=np.int64)
+    busy = rng.choice(E, size=min(E, 300), replace=False)
+    counts[busy] = rng.integers(1, 40, size=busy.size)
+    counts[busy[:6]] = [128, 256, 300, 513, 700, 1]  # whole tiles of every height, and past them
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    R = int(offsets[-1])
+    a_rows = 900
+    src = rng.integers(0, a_rows, size=R).astype(np.int32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(E + epi)
+    a = _rand_nvfp4(gen, (a_rows, H), dev)
+    w = _rand_nvfp4(gen, (E, N, H), dev)
+    out_dtype = torch.bfloat16 if out == "bf16" else torch.float32
+    got = B.nvfp4_moe_grouped_gemm(a, torch.from_numpy(src).to(dev),
+                                   torch.from_numpy(offsets.astype(np.int32)).to(dev), R, w,
+                                   epilogue=epi, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check_grouped(B, a, w, got, offsets, src, [int(e) for e in np.flatnonzero(counts)], epi, out_dtype,
+                   f"offsets E={E} R={R} epi={epi} out={out}")
+
+
+@pytest.mark.parametrize("layout", ["last", "first", "none"])
+def test_grouped_gemm_edge_segments(B, layout):
+    """All rows in the last of 700 experts (the scan's last thread holds them),
+    all in the first of 5, and no routed rows at all (R = 0: nothing is written,
+    the call succeeds)."""
+    dev = "cuda"
+    H, N = 512, 256
+    E = 700 if layout == "last" else 5
+    counts = np.zeros(E, dtype=np.int64)
+    if layout == "last":
+        counts[-1] = 333
+    elif layout == "first":
+        counts[0] = 1000
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    R = int(offsets[-1])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(E)
+    a = _rand_nvfp4(gen, (max(R, 1), H), dev)
+    w = _rand_nvfp4(gen, (E, N, H), dev)
+    got = B.nvfp4_moe_grouped_gemm(a, None, torch.from_numpy(offsets.astype(np.int32)).to(dev), R, w,
+                                   out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (R, N)
+    if R:
+        _check_grouped(B, a, w, got, offsets, np.arange(R), [int(np.flatnonzero(counts)[0])], 0,
+                       torch.bfloat16, f"edge segments {layout} E={E} R={R}")
 
 
 @pytest.mark.parametrize("H,I", [(256, 128), (2048, 768)])
