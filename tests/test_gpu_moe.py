@@ -407,6 +407,51 @@ def test_gate_up_nvfp4_epilogue(B, T, E, k, H, I, g_div):
           f"{int((s_ref == 0x7E).sum())} blocks at scale 448", flush=True)
 
 
+@pytest.mark.parametrize("epi,out", [(0, "f32"), (1, "bf16"), (1, "nvfp4")])
+def test_grouped_rows_past_offsets_untouched(B, epi, out):
+    """R is only an upper bound on offsets[E]: the launch is sized by R, rows
+    [offsets[E], R) of the output keep what they held, and the rows before them
+    are what the exact-size call computes (checked against the oracle)."""
+    dev = "cuda"
+    T, E, k, H, I = 300, 9, 2, 512, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31 + epi)
+    r = B.nvfp4_moe_route(_routing(gen, T, E, k, dev, skew=True), k)
+    n = T * k
+    R = n + 77
+    a = _rand_nvfp4(gen, (T, H), dev)
+    N = 2 * I if epi else I
+    w = _rand_nvfp4(gen, (E, N, H), dev)
+    offsets = _np(r["offsets"]).astype(np.int64)
+    assert offsets[-1] == n
+    if out == "nvfp4":
+        h32 = B.nvfp4_moe_grouped_gemm(a, r["src_row"], r["offsets"], n, w,
+                                       epilogue=B.NVFP4_EPI_SILU_GATE, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check_grouped(B, a, w, h32, offsets, _np(r["src_row"]), range(E), epi, torch.float32,
+                       f"rows past offsets, h in float32 (R = {n})")
+        h_np = _np(h32).astype(np.float32)
+        g_h = np.float32(OQ.global_scale(h_np))
+        hq = torch.full((R, I // 2), 0xAB, dtype=torch.uint8, device=dev)
+        hs = torch.full((R, I // 16), 0xCD, dtype=torch.uint8, device=dev)
+        B.nvfp4_moe_grouped_gemm_silu_nvfp4(a, r["src_row"], r["offsets"], R, w,
+                                            torch.tensor([float(g_h)], device=dev), out=(hq, hs))
+        torch.cuda.synchronize()
+        q_ref, s_ref, _ = OQ.quantize(h_np, g=g_h)
+        np.testing.assert_array_equal(_np(hq[:n]), q_ref)
+        np.testing.assert_array_equal(_np(hs[:n]), s_ref)
+        assert bool((hq[n:] == 0xAB).all()) and bool((hs[n:] == 0xCD).all())
+        return
+    out_dtype = torch.bfloat16 if out == "bf16" else torch.float32
+    c = torch.full((R, I), float("nan"), dtype=out_dtype, device=dev)
+    B.nvfp4_moe_grouped_gemm(a, r["src_row"], r["offsets"], R, w, epilogue=epi, out_dtype=out_dtype, out=c)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(c[n:]).all())
+    assert not bool(torch.isnan(c[:n]).any())
+    _check_grouped(B, a, w, c, offsets, _np(r["src_row"]), range(E), epi, out_dtype,
+                   f"rows past offsets epi={epi} out={out} (R = {R}, offsets[E] = {n})")
+
+
 def test_gate_up_nvfp4_epilogue_unsupported_layout(B):
     # K % 256 != 0: the fused path reports "unsupported" instead of running
     dev = "cuda"
