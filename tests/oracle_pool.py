@@ -154,6 +154,43 @@ def silu_gate_block_check(a, b, h, out_bf16):
     return _stats(h, ref, err, out_bf16)
 
 
+# ----------------------------------------------------------------------- FP8
+
+
+def _fp8_encode_chunk(x, g):
+    from oracle import fp8 as P
+    return P.encode(x, g)
+
+
+def fp8_encode_rows(x, g, rows_per_task=None):
+    """The FP8 oracle's E4M3 codes of float32 x [rows, cols] under the
+    per-tensor scale g, by row blocks."""
+    rows = x.shape[0]
+    if rows_per_task is None:
+        rows_per_task = max(1, min(rows, (4 << 20) // max(1, x.shape[1])))
+    futs = [pool().submit(_fp8_encode_chunk, np.ascontiguousarray(x[r:r + rows_per_task]), g)
+            for r in range(0, rows, rows_per_task)]
+    return np.concatenate([f.result() for f in futs])
+
+
+def fp8_gemm_block_check(a, b, y, out_bf16):
+    """Oracle FP8 GEMM of a = (q, g) [m, K] and b = (q, g) [n, K] (E4M3 codes,
+    per-tensor scales) against the GPU's y [m, n]; returns _stats.  Bound: the
+    products of two E4M3 values are exact in float32, but unlike the NVFP4
+    products (few-bit values whose sums stay exact) their sums round.  However
+    the matrix core orders the sum, each of its K additions rounded to float32
+    errs by at most one unit in the last place of a partial sum bounded by
+    sum_k |a_k b_k| (2 U relative, whatever the rounding mode), and the
+    epilogue's scaling by a_g b_g adds a few roundings more: 2 (K + 20) U
+    ||a|| ||b||."""
+    from oracle import fp8 as P
+    ref = P.gemm(*a, *b)
+    K = a[0].shape[1]
+    na = np.sqrt((P.dequantize(*a) ** 2).sum(axis=1))
+    nb = np.sqrt((P.dequantize(*b) ** 2).sum(axis=1))
+    return _stats(y, ref, 2 * (K + 20) * U * np.outer(na, nb), out_bf16)
+
+
 def run(fn, tasks):
     """Submit fn(*task) for every task; results in task order."""
     futs = [pool().submit(fn, *t) for t in tasks]

@@ -8,6 +8,8 @@
   operands; relative Frobenius error <= 1e-3 against the oracle rounded to
   bf16, and every element within the float32 accumulation bound plus one bf16
   unit (oracle_pool's module docstring states the bound).
+* FP8 W8A8 on the prefill workload: E4M3 codes and per-tensor scales of X and
+  W bit-exact, the whole bf16 GEMM output within its float32 summation bound.
 * MoE (128 experts top-8, 512 experts top-10), stage by stage, each stage given
   the GPU's own input to it (the float32/bf16 h and y are computed in a
   different precision than the oracle's float64 ones, so a downstream code may
@@ -121,6 +123,41 @@ def test_lmhead_128x151936_full(B):
     wg, wr = _quantize_exact(B, w, "lm_head W")
     del x, w
     _gemm_full(B, xg, wg, xr, wr, 128, 9496, "lm_head GEMM 128x151936x2048 bf16")
+
+
+def test_fp8_prefill_8192x5120_full(B):
+    """FP8 W8A8 on the prefill workload, every element: the GPU's E4M3 codes and
+    per-tensor scales of X and W bit-exact against the oracle's over the whole
+    tensors, and the whole bf16 GEMM output against the oracle's float64 product
+    of those operands (relative Frobenius error and the element bound of
+    oracle_pool.fp8_gemm_block_check)."""
+    from oracle import fp8 as P
+    x, w = W.linear_inputs("prefill_8192x5120", device="cuda")
+    gpu, ref = [], []
+    for t, label in ((x, "X"), (w, "W")):
+        t0 = time.time()
+        q, g = B.nvfp4_fp8_quantize(t)
+        torch.cuda.synchronize()
+        th = _host(t)
+        gr = P.scale(th)
+        assert g.item() == gr, label
+        rq = OP.fp8_encode_rows(th, gr)
+        np.testing.assert_array_equal(_np(q), rq, err_msg=label)
+        _log(f"FP8 prefill {label} {tuple(t.shape)}: codes and scale bit-exact", t0)
+        gpu.append((q, g))
+        ref.append((rq, gr))
+        del th
+    del x, w
+    t0 = time.time()
+    y = B.nvfp4_fp8_gemm(gpu[0], gpu[1], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    yh = _host(y)
+    M, N = yh.shape
+    tasks = [((ref[0][0][r:r + 1024], ref[0][1]), (ref[1][0][c:c + 3200], ref[1][1]),
+              np.ascontiguousarray(yh[r:r + 1024, c:c + 3200]), True)
+             for r in range(0, M, 1024) for c in range(0, N, 3200)]
+    _assert_stats(OP.merge(OP.run(OP.fp8_gemm_block_check, tasks)), "FP8 prefill GEMM 8192x25600x5120 bf16")
+    _log("FP8 prefill GEMM checked", t0)
 
 
 # ----------------------------------------------------------------------- MoE
