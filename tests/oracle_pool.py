@@ -78,6 +78,22 @@ def quantize_rows(x, g, rows_per_task=None):
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
+def _qdq_chunk(x, g, out):
+    from oracle import qdq as D
+    return D.qdq(x, g=g, out=out)[0]
+
+
+def qdq_rows(x, g, out, rows_per_task=None):
+    """The oracle's quantize-dequantize of float32 x [rows, cols] under global
+    scale g ("f32" or "bf16" values), by row blocks."""
+    rows = x.shape[0]
+    if rows_per_task is None:
+        rows_per_task = max(1, min(rows, (4 << 20) // max(1, x.shape[1])))
+    futs = [pool().submit(_qdq_chunk, np.ascontiguousarray(x[r:r + rows_per_task]), g, out)
+            for r in range(0, rows, rows_per_task)]
+    return np.concatenate([f.result() for f in futs])
+
+
 # ---------------------------------------------------------------------- GEMM
 
 

@@ -8,6 +8,8 @@
   operands; relative Frobenius error <= 1e-3 against the oracle rounded to
   bf16, and every element within the float32 accumulation bound plus one bf16
   unit (oracle_pool's module docstring states the bound).
+* Quantize-dequantize of the prefill X and W (single-read and two-pass
+  paths), every value bit-exact.
 * FP8 W8A8 on the prefill workload: E4M3 codes and per-tensor scales of X and
   W bit-exact, the whole bf16 GEMM output within its float32 summation bound.
 * MoE (128 experts top-8, 512 experts top-10), stage by stage, each stage given
@@ -123,6 +125,25 @@ def test_lmhead_128x151936_full(B):
     wg, wr = _quantize_exact(B, w, "lm_head W")
     del x, w
     _gemm_full(B, xg, wg, xr, wr, 128, 9496, "lm_head GEMM 128x151936x2048 bf16")
+
+
+@pytest.mark.parametrize("which", ["X", "W"])
+def test_qdq_prefill_full(B, which):
+    """Quantize-dequantize of the whole prefill X (8192x5120, the single-read
+    path) and W (25600x5120, beyond the register capacity: the two-pass path),
+    bf16 values and global scale bit-exact against the oracle."""
+    x, w = W.linear_inputs("prefill_8192x5120", device="cuda")
+    t = x if which == "X" else w
+    del x, w
+    t0 = time.time()
+    y, g = B.nvfp4_qdq(t)
+    torch.cuda.synchronize()
+    th = _host(t)
+    rg = Q.global_scale(th)
+    assert g.item() == rg
+    ref = OP.qdq_rows(th, rg, "bf16")
+    np.testing.assert_array_equal(_host(y), ref)
+    _log(f"QDQ prefill {which} {tuple(t.shape)}: every value bit-exact", t0)
 
 
 def test_fp8_prefill_8192x5120_full(B):
