@@ -94,6 +94,25 @@ def qdq_rows(x, g, out, rows_per_task=None):
     return np.concatenate([f.result() for f in futs])
 
 
+def _four6_chunk(x, g):
+    from oracle import four_over_six as F
+    q, s, _, took4 = F.quantize(x, g=g)
+    return q, s, int(took4.sum())
+
+
+def four_over_six_rows(x, g, rows_per_task=None):
+    """The four-over-six oracle's (q, s) of float32 x [rows, cols] under global
+    scale g, by row blocks, and how many blocks took the scale of 4."""
+    rows = x.shape[0]
+    if rows_per_task is None:
+        rows_per_task = max(1, min(rows, (4 << 20) // max(1, x.shape[1])))
+    futs = [pool().submit(_four6_chunk, np.ascontiguousarray(x[r:r + rows_per_task]), g)
+            for r in range(0, rows, rows_per_task)]
+    parts = [f.result() for f in futs]
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            sum(p[2] for p in parts))
+
+
 # ---------------------------------------------------------------------- GEMM
 
 

@@ -10,6 +10,8 @@
   unit (oracle_pool's module docstring states the bound).
 * Quantize-dequantize of the prefill X and W (single-read and two-pass
   paths), every value bit-exact.
+* Four-over-six offline quantize of the prefill and lm_head weights, every
+  code and scale bit-exact.
 * FP8 W8A8 on the prefill workload: E4M3 codes and per-tensor scales of X and
   W bit-exact, the whole bf16 GEMM output within its float32 summation bound.
 * MoE (128 experts top-8, 512 experts top-10), stage by stage, each stage given
@@ -144,6 +146,25 @@ def test_qdq_prefill_full(B, which):
     ref = OP.qdq_rows(th, rg, "bf16")
     np.testing.assert_array_equal(_host(y), ref)
     _log(f"QDQ prefill {which} {tuple(t.shape)}: every value bit-exact", t0)
+
+
+@pytest.mark.parametrize("name", ["prefill_8192x5120", "lmhead_128x151936"])
+def test_four_over_six_weights_full(B, name):
+    """Four-over-six offline quantize of the whole weight matrix of the prefill
+    (25600x5120) and lm_head (151936x2048) workloads: codes, block scales and
+    global scale bit-exact against the oracle."""
+    _, w = W.linear_inputs(name, device="cuda")
+    t0 = time.time()
+    q, s, g = B.nvfp4_quantize_4over6(w)
+    torch.cuda.synchronize()
+    wh = _host(w)
+    rg = Q.global_scale(wh)
+    assert g.item() == rg
+    rq, rs, took4 = OP.four_over_six_rows(wh, rg)
+    np.testing.assert_array_equal(_np(s), rs)
+    np.testing.assert_array_equal(_np(q), rq)
+    _log(f"four-over-six {name} W {tuple(w.shape)}: codes, scales, global scale bit-exact; "
+         f"{took4 / rs.size:.1%} of blocks take the scale of 4", t0)
 
 
 def test_fp8_prefill_8192x5120_full(B):
