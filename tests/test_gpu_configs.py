@@ -8,6 +8,8 @@
   operands; relative Frobenius error <= 1e-3 against the oracle rounded to
   bf16, and every element within the float32 accumulation bound plus one bf16
   unit (oracle_pool's module docstring states the bound).
+* Static-scale quantize of the prefill X (a calibrated scale, and one that
+  saturates), every code and scale bit-exact.
 * Quantize-dequantize of the prefill X and W (single-read and two-pass
   paths), every value bit-exact.
 * Four-over-six offline quantize of the prefill and lm_head weights, every
@@ -127,6 +129,26 @@ def test_lmhead_128x151936_full(B):
     wg, wr = _quantize_exact(B, w, "lm_head W")
     del x, w
     _gemm_full(B, xg, wg, xr, wr, 128, 9496, "lm_head GEMM 128x151936x2048 bf16")
+
+
+@pytest.mark.parametrize("g_div", [1.0, 64.0])
+def test_static_quantize_prefill_full(B, g_div):
+    """Static-scale quantize of the whole prefill X (8192x5120 bf16) under a
+    calibrated global scale: the tensor's own amax/2688, and that scale / 64
+    (blocks whose scale saturates at 448, codes at 6): codes and scales
+    bit-exact against the oracle."""
+    x, _ = W.linear_inputs("prefill_8192x5120", device="cuda")
+    t0 = time.time()
+    xh = _host(x)
+    g = np.float32(Q.global_scale(xh) / np.float32(g_div))
+    q, s, gg = B.nvfp4_quantize(x, g=torch.tensor([float(g)], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert gg.item() == g
+    rq, rs = OP.quantize_rows(xh, g)
+    np.testing.assert_array_equal(_np(s), rs)
+    np.testing.assert_array_equal(_np(q), rq)
+    _log(f"static quantize prefill X, g = amax/2688/{g_div:g}: codes and scales bit-exact, "
+         f"{int((rs == 0x7E).sum()):,} blocks at scale 448", t0)
 
 
 @pytest.mark.parametrize("which", ["X", "W"])
