@@ -8,6 +8,8 @@
   operands; relative Frobenius error <= 1e-3 against the oracle rounded to
   bf16, and every element within the float32 accumulation bound plus one bf16
   unit (oracle_pool's module docstring states the bound).
+* Dynamic quantize at the single-read path's capacity and one row past it
+  (the two-pass path), bf16 and float32, every code and scale bit-exact.
 * Static-scale quantize of the prefill X (a calibrated scale, and one that
   saturates), every code and scale bit-exact.
 * Quantize-dequantize of the prefill X and W (single-read and two-pass
@@ -129,6 +131,43 @@ def test_lmhead_128x151936_full(B):
     wg, wr = _quantize_exact(B, w, "lm_head W")
     del x, w
     _gemm_full(B, xg, wg, xr, wr, 128, 9496, "lm_head GEMM 128x151936x2048 bf16")
+
+
+# The single-read (register-resident) dynamic quantize holds at most one
+# workgroup per compute unit, 512 threads each, 20 bf16 or 10 float32 blocks per
+# thread; one block more takes the two-pass path.  Its workspace's first word
+# is the parity the single-read kernel flips on every call, so a test sees
+# which path ran.
+@pytest.mark.parametrize("case", ["bf16 at capacity", "bf16 one row past", "f32 at capacity",
+                                  "f32 one row past", "f32 32768x768"])
+def test_quantize_single_read_capacity(B, case):
+    bf16 = case.startswith("bf16")
+    cols = 5120 if bf16 else 1024
+    cus = min(torch.cuda.get_device_properties(0).multi_processor_count, 1024)
+    cap_rows = cus * 512 * (20 if bf16 else 10) * 16 // cols
+    rows = {"at capacity": cap_rows, "one row past": cap_rows + 1}.get(case.split(" ", 1)[1], 32768)
+    if case == "f32 32768x768":
+        cols = 768
+    single_read = rows * cols // 16 <= cus * 512 * (20 if bf16 else 10)
+    x = W.random_matrix(rows, cols, seed=rows + cols, dtype=torch.bfloat16 if bf16 else torch.float32,
+                        device="cuda")
+    t0 = time.time()
+    B.nvfp4_quantize(x)  # the stream's workspace has its final size before its parity is read
+    torch.cuda.synchronize()
+    ws = B._QWS[(torch.cuda.current_device(), int(torch.cuda.current_stream().cuda_stream))]
+    before = int(ws[0:4].view(torch.int32).item())
+    q, s, g = B.nvfp4_quantize(x)
+    torch.cuda.synchronize()
+    flipped = int(ws[0:4].view(torch.int32).item()) != before
+    assert flipped == single_read, (case, rows, cols, flipped)
+    xh = _host(x)
+    rg = Q.global_scale(xh)
+    assert g.item() == rg
+    rq, rs = OP.quantize_rows(xh, rg)
+    np.testing.assert_array_equal(_np(s), rs)
+    np.testing.assert_array_equal(_np(q), rq)
+    _log(f"quantize {case} ({rows}x{cols}): {'single-read' if single_read else 'two-pass'} path, "
+         f"codes, scales, global scale bit-exact", t0)
 
 
 @pytest.mark.parametrize("g_div", [1.0, 64.0])

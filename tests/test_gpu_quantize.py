@@ -211,8 +211,9 @@ def test_two_pass_path_large_bf16(B):
     _sampled(B, x, rows)
 
 
-def test_resident_fp32_at_capacity(B):
-    """fp32 h of the 128-expert MoE (32768 x 768) fills the resident path exactly."""
+def test_fp32_moe_h_two_pass(B):
+    """float32 h of the 128-expert MoE (32768 x 768): 1.2 times what the
+    single-read path holds (10 float32 blocks per thread), so the two-pass path."""
     x = W.random_matrix(32768, 768, seed=22, device="cuda")
     rows = torch.tensor([0, 32767] + list(range(3, 32768, 1021)), device="cuda")
     _sampled(B, x, rows)
