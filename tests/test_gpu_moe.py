@@ -72,6 +72,15 @@ def test_route_small(B, T, E, k):
     _check_route(B, logits, k)
 
 
+# Many tokens: the counting sort's per-group counts (64 tokens a group) span
+# 1,563 and 625 groups, past the scan's 32-deep load batches; k up to the
+# maximum of 32 with 1024 experts.
+@pytest.mark.parametrize("T,E,k", [(100000, 64, 4), (40000, 1024, 32), (65537, 7, 7)])
+def test_route_many_tokens(B, T, E, k):
+    logits = W.random_matrix(T, E, seed=T + E + k, device="cuda")
+    _check_route(B, logits, k)
+
+
 def test_route_ties_and_signed_zero(B):
     logits = torch.zeros((70, 9), device="cuda")
     logits[3] = 1.0
