@@ -478,7 +478,10 @@ def test_gate_up_nvfp4_epilogue_unsupported_layout(B):
 # ---------------------------------------------------------------- combine
 
 
-@pytest.mark.parametrize("T,k,H", [(1, 1, 16), (100, 8, 2048), (33, 10, 4096 + 64)])
+# H % 8 != 0 (100, 1029) takes the one-element-per-thread path, the others the
+# 8-wide vector path; k up to 32
+@pytest.mark.parametrize("T,k,H", [(1, 1, 16), (100, 8, 2048), (33, 10, 4096 + 64), (7, 32, 100),
+                                   (1000, 3, 1029)])
 @pytest.mark.parametrize("y_bf16", [False, True])
 def test_combine(B, T, k, H, y_bf16):
     gen = torch.Generator(device="cuda")
@@ -496,6 +499,13 @@ def test_combine(B, T, k, H, y_bf16):
     assert err <= TOL, err
     out32 = B.nvfp4_moe_combine(y, w, inv, out_dtype=torch.float32)
     np.testing.assert_allclose(_np(out32), ref, rtol=1e-5, atol=1e-5)
+    # float32 output: exactly the arithmetic the entry point states, slot by
+    # slot, each product and each addition rounded once to float32
+    yf, wf, iv = _np(y.float()), _np(w), _np(inv)
+    acc = np.zeros((T, H), dtype=np.float32)
+    for j in range(k):
+        acc = acc + wf[:, j:j + 1] * yf[iv[:, j]]
+    np.testing.assert_array_equal(_np(out32), acc)
 
 
 def test_combine_bf16_output_is_rounded_f32_output(B):
