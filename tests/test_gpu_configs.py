@@ -29,7 +29,8 @@
   bound); the quantize of h bit-exact against the oracle's quantize of the
   GPU's h (whole tensor); down per checked expert against the oracle on the
   oracle's quantize of the GPU's h; the combine against the oracle's combine of
-  the GPU's y and routing weights.  Both storage types of h and y (bf16, as
+  the GPU's y and routing weights (and bit-exact against its stated float32
+  slot order rounded to bf16).  Both storage types of h and y (bf16, as
   the benchmark runs, and float32).  With float32 h, the gate_up's fused NVFP4
   epilogue (static global scale) is checked bit-exact as well.
 
@@ -49,6 +50,7 @@ import torch
 import oracle_pool as OP
 from oracle import moe as OM
 from oracle import nvfp4 as Q
+from oracle import qdq as OD
 from moe_nvfp4_quantize_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -406,7 +408,14 @@ def test_moe_stagewise(B, name, inter):
     err = 2 * k * OP.U * mag
     stc = OP.merge([OP._stats(_host(out), ref, err, True)])
     _assert_stats(stc, f"{name} {inter}: combine {T}x{H} bf16")
-    _log("combine checked", t0)
+    # and bit for bit the arithmetic the entry point states: slots in order,
+    # each float32 product and addition rounded once, then bf16 (nearest even)
+    y32, w32 = yh.astype(np.float32), _np(r["topk_w"])
+    acc = np.zeros((T, H), dtype=np.float32)
+    for j in range(k):
+        acc = acc + w32[:, j:j + 1] * y32[st["inv"][:, j]]
+    np.testing.assert_array_equal(_host(out), OD.round_to_bf16(acc))
+    _log("combine checked (and bit-exact to its float32 slot order)", t0)
 
     if inter == "f32":
         # the fused SiLU-gate -> NVFP4 epilogue under a static scale: bit-exact
