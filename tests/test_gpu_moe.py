@@ -461,6 +461,33 @@ def test_grouped_rows_past_offsets_untouched(B, epi, out):
                    f"rows past offsets epi={epi} out={out} (R = {R}, offsets[E] = {n})")
 
 
+@pytest.mark.parametrize("epi,out", [(0, "f32"), (0, "bf16"), (1, "bf16"), (1, "f32")])
+def test_grouped_output_independent_of_tile_height(B, epi, out):
+    """R, the host's upper bound on offsets[E], sizes the launch, and the
+    launcher picks the tile height from R / E: the same 1000 routed rows over 16
+    experts computed with R = 1000, 2400 and 3200 run 128-, 192- and 256-row
+    tiles (the first two, without the gate, with the two-tile walk), and the
+    rows come out bit-identical, each output's sum over K taken in the same
+    order at every height.  The first run is checked against the oracle."""
+    dev = "cuda"
+    T, E, k, H = 1000, 16, 1, 1024
+    N = 1024 if epi else 512
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(57 + epi)
+    r = B.nvfp4_moe_route(_routing(gen, T, E, k, dev, skew=True), k)
+    a = _rand_nvfp4(gen, (T, H), dev)
+    w = _rand_nvfp4(gen, (E, N, H), dev)
+    out_dtype = torch.bfloat16 if out == "bf16" else torch.float32
+    n = T * k
+    outs = [B.nvfp4_moe_grouped_gemm(a, r["src_row"], r["offsets"], R, w, epilogue=epi,
+                                     out_dtype=out_dtype)[:n] for R in (n, 150 * E, 200 * E)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    _check_grouped(B, a, w, outs[0], _np(r["offsets"]).astype(np.int64), _np(r["src_row"]), range(E),
+                   epi, out_dtype, f"tile heights 128 / 192 / 256, epi={epi} out={out}")
+
+
 def test_gate_up_nvfp4_epilogue_unsupported_layout(B):
     # K % 256 != 0: the fused path reports "unsupported" instead of running
     dev = "cuda"
