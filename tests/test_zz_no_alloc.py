@@ -7,7 +7,8 @@ input, so the second reuses the per-GPU scratch the first left behind: the
 first takes the two-pass path (more blocks than the register file holds: its
 amax partials live in the scratch), the second the single-read path (its
 arrival state lives there); then the same again in float32, and a static
-global scale.
+global scale.  Under HIP graph capture: replays of a captured call match the
+entry point on each replay's input.
 """
 
 import numpy as np
@@ -65,6 +66,31 @@ def test_noalloc_static_scale_and_repeats(B):
     for i in range(3):  # the arrival state left by each call serves the next
         xi = x[: 512 - 100 * i] * (i + 1.0)
         _same(_noalloc_abi(B, xi), B.nvfp4_quantize(xi), ("repeat", i))
+
+
+@pytest.mark.parametrize("shape", [(1000, 2048), (8192, 6144)])  # single-read, two-pass path
+def test_noalloc_under_graph_capture(B, shape):
+    """Captured in a HIP graph (the callers it serves) after one eager call has
+    set up the GPU's scratch, then replayed three times with the input rewritten
+    in place and eager work between the replays (the workspace entry point on
+    the same input): every replay bit-identical to that entry point."""
+    r, c = shape
+    x = W.random_matrix(r, c, seed=960, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((r, c // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty((r, c // 16), dtype=torch.uint8, device="cuda")
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    B.nvfp4_quantize_noalloc(x, out=(q, s, g))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.nvfp4_quantize_noalloc(x, out=(q, s, g))
+    torch.cuda.synchronize()
+    for i in range(3):
+        print(f"[noalloc] graph replay {i}: {r}x{c} bf16", flush=True)
+        x.copy_(W.random_matrix(r, c, seed=961 + i, dtype=torch.bfloat16, device="cuda") * (1.0 + 3 * i))
+        want = B.nvfp4_quantize(x)
+        graph.replay()
+        _same((q, s, g), want, ("replay", i, shape))
 
 
 def test_noalloc_rejects_invalid(B):
