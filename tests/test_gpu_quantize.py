@@ -60,6 +60,21 @@ def test_strided_rows_take_the_unaligned_path(B):
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("rows,cols,dtype", [(300, 1024, torch.bfloat16), (100, 512, torch.float32),
+                                             (8200, 6144, torch.bfloat16)])
+def test_misaligned_base_takes_the_unaligned_path(B, rows, cols, dtype):
+    """Dense rows starting one element past a 16-byte boundary: accepted and
+    quantized by the unaligned path (single-read for the first two shapes,
+    two-pass for the last), bit-exact."""
+    flat = W.random_matrix(1, rows * cols + 8, seed=rows + cols, dtype=dtype, device="cuda").view(-1)
+    x = flat[1:1 + rows * cols].view(rows, cols)
+    assert x.data_ptr() % 16 != 0
+    if rows * cols > 10_000_000:
+        _sampled(B, x, torch.tensor([0, 1, rows // 2, rows - 1] + list(range(7, rows, 997)), device="cuda"))
+    else:
+        _check_full(B, x)
+
+
 def test_degenerate_values(B):
     z = torch.zeros((4, 64), device="cuda")
     _check_full(B, z)
