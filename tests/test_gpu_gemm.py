@@ -140,6 +140,34 @@ def test_ragged_shapes(B, M, N, K, out_dtype):
     _compare(y, G.gemm(*a, *b), out_dtype, f"ragged {M}x{N}x{K}", operands=(a, b))
 
 
+def _up_at(t, q_off, s_off):
+    """Upload (q, s, g) with q and s starting q_off and s_off bytes past a
+    16-byte boundary (dense rows)."""
+    q, s, g = t
+
+    def place(a, off):
+        flat = torch.empty(a.size + 32, dtype=torch.uint8, device="cuda")
+        base = (-flat.data_ptr()) % 16 + off
+        v = flat[base:base + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+        assert v.data_ptr() % 16 == off
+        return v
+    return place(q, q_off), place(s, s_off), torch.tensor([float(g)], dtype=torch.float32, device="cuda")
+
+
+# Operands off the 16-byte (codes) or 8-byte (scales) alignment the direct-to-
+# LDS kernel needs: accepted, and computed by the general kernel.
+@pytest.mark.parametrize("which", ["a codes", "b scales", "all"])
+@pytest.mark.parametrize("M,N,K", [(130, 300, 512), (64, 256, 1024)])
+def test_misaligned_operands(B, which, M, N, K):
+    rng = np.random.default_rng(M + N + K + len(which))
+    a = _random_nvfp4(rng, M, K, 2.0 ** -6)
+    b = _random_nvfp4(rng, N, K, 2.0 ** -7)
+    offs = {"a codes": ((1, 0), (0, 0)), "b scales": ((0, 0), (0, 3)), "all": ((5, 1), (9, 2))}[which]
+    y = B.nvfp4_gemm(_up_at(a, *offs[0]), _up_at(b, *offs[1]), out_dtype=torch.float32)
+    _compare(y, G.gemm(*a, *b), torch.float32, f"misaligned {which} {M}x{N}x{K}", operands=(a, b))
+
+
 def _random_nvfp4(rng, rows, K, g):
     """Operands straight in the format: any code byte, block scales from 0.25
     to 15 (E4M3 codes 0x28 .. 0x57)."""
